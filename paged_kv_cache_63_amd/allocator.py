@@ -1,0 +1,239 @@
+"""Host-side block manager for the paged KV cache.
+
+The pages put this layer on the host: a per-sequence block table, a pool of
+interchangeable physical blocks, allocation one block at a time when the last
+block is full, sharing by reference count, and copy-on-write when a shared
+block is about to change ("Paged Attention for Efficient Memory Management",
+The Daily Triptych, technical summary and "Look closer"; "PagedAttention 与
+RadixAttention", section "PagedAttention"; "PagedAttention and
+RadixAttention: Let's Talk About KV Cache", section "PagedAttention: Memory
+Like an Operating System").
+
+State lives in flat numpy arrays so a decode step over a whole batch is a few
+vector operations:
+
+* ``tables``  int32 ``[max_seqs][max_blocks_per_seq]``; row = sequence id;
+  entries past the sequence's block count are ``-1``.  A slice of rows is
+  exactly the ``block_tables`` argument the device calls take.
+* ``lens``    int32 ``[max_seqs]`` tokens written per sequence.
+* ``ref``     int32 ``[num_blocks]`` references per physical block.
+
+Rules where the pages leave a choice (the oracle's block-manager model fixes
+the same ones, and the tests compare the two token for token):
+
+* The free list is FIFO: the oldest free block is handed out first; a block
+  whose count reaches zero goes to the back.  The initial order is the
+  caller's (``free_order``).
+* A sequence that writes into a partly filled block still shared with others
+  gets a fresh block and a ``(src, dst)`` pair for :func:`copy_blocks`; the
+  last owner writes in place.  Within one call the copy destination is taken
+  before any new block.
+* A sequence holds ``ceil(len / B)`` blocks, so at most ``B - 1`` slots of
+  one partly filled block are idle (the waste bound of the pages).
+"""
+
+from collections import deque
+
+import numpy as np
+
+
+class OutOfBlocks(RuntimeError):
+    """Raised when an operation needs more free blocks than the pool has.
+    The allocator state is left unchanged."""
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int,
+                       elem_bytes: int) -> int:
+    """Bytes of KV cache one token occupies across a model: a key and a value
+    vector per KV head per layer.  ("PagedAttention and RadixAttention: Let's
+    Talk About KV Cache", opening section, gives about 0.31 MB per token for
+    Llama-3.1-70B in BF16.)"""
+    return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
+
+
+class BlockAllocator:
+    def __init__(self, num_blocks: int, block_size: int = 16, max_seqs: int = 256,
+                 max_blocks_per_seq: int = None, free_order=None):
+        if num_blocks <= 0 or block_size <= 0 or max_seqs <= 0:
+            raise ValueError("num_blocks, block_size and max_seqs must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        self.max_seqs = int(max_seqs)
+        self.max_blocks_per_seq = int(max_blocks_per_seq or num_blocks)
+        self.tables = np.full((self.max_seqs, self.max_blocks_per_seq), -1, dtype=np.int32)
+        self.lens = np.zeros(self.max_seqs, dtype=np.int32)
+        self.nblk = np.zeros(self.max_seqs, dtype=np.int32)
+        self.ref = np.zeros(self.num_blocks, dtype=np.int32)
+        self.live = np.zeros(self.max_seqs, dtype=bool)
+        order = np.arange(self.num_blocks) if free_order is None else np.asarray(free_order)
+        if sorted(int(b) for b in order) != list(range(self.num_blocks)):
+            raise ValueError("free_order must be a permutation of range(num_blocks)")
+        self._free = deque(int(b) for b in order)
+        self._rows = deque(range(self.max_seqs))
+
+    # ---------------------------------------------------------------- blocks
+    def _take(self, n: int) -> np.ndarray:
+        out = np.fromiter((self._free.popleft() for _ in range(n)), dtype=np.int32, count=n)
+        self.ref[out] = 1
+        return out
+
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def refcount(self, block: int) -> int:
+        return int(self.ref[block])
+
+    # ------------------------------------------------------------- sequences
+    def new_seq(self) -> int:
+        if not self._rows:
+            raise RuntimeError("no free sequence row (max_seqs reached)")
+        sid = self._rows.popleft()
+        self.live[sid] = True
+        self.lens[sid] = 0
+        self.nblk[sid] = 0
+        return sid
+
+    def _check(self, sid: int) -> None:
+        if not (0 <= sid < self.max_seqs) or not self.live[sid]:
+            raise KeyError(f"sequence {sid} is not live")
+
+    def append_tokens(self, sid: int, n: int):
+        """Reserve slots for ``n`` more tokens of one sequence.
+
+        Returns ``(slots int32[n], pairs int32[k][2])``: the pool slot of each
+        new token, in order, and the copy-on-write pairs that must be copied
+        on the device before the tokens are written.
+        """
+        self._check(sid)
+        B = self.block_size
+        pos0 = int(self.lens[sid])
+        nb = int(self.nblk[sid])
+        pairs = np.zeros((0, 2), dtype=np.int32)
+        if n <= 0:
+            return np.zeros(0, dtype=np.int32), pairs
+        cow = pos0 % B != 0 and self.ref[self.tables[sid, nb - 1]] > 1
+        new = -(-(pos0 + n) // B) - nb
+        if int(cow) + new > len(self._free):
+            raise OutOfBlocks(f"need {int(cow) + new} blocks, {len(self._free)} free")
+        if nb + new > self.max_blocks_per_seq:
+            raise ValueError("sequence would exceed max_blocks_per_seq")
+        if cow:
+            src = int(self.tables[sid, nb - 1])
+            dst = int(self._take(1)[0])
+            self.ref[src] -= 1
+            self.tables[sid, nb - 1] = dst
+            pairs = np.array([[src, dst]], dtype=np.int32)
+        if new:
+            self.tables[sid, nb:nb + new] = self._take(new)
+            self.nblk[sid] = nb + new
+        pos = np.arange(pos0, pos0 + n)
+        slots = self.tables[sid, pos // B].astype(np.int64) * B + pos % B
+        self.lens[sid] = pos0 + n
+        return slots.astype(np.int32), pairs
+
+    def append_step(self, sids):
+        """One new token for each sequence in ``sids`` (a decode step), handled
+        in the order given.  Same result as ``append_tokens(s, 1)`` for each
+        ``s`` in turn, done with whole-batch array operations.
+
+        Returns ``(slots int32[len(sids)], pairs int32[k][2])``.
+        """
+        sids = np.asarray(sids, dtype=np.int64)
+        if len(np.unique(sids)) != len(sids):
+            raise ValueError("a sequence may appear once per step")
+        if not self.live[sids].all():
+            raise KeyError("append_step on a sequence that is not live")
+        B = self.block_size
+        pos = self.lens[sids].astype(np.int64)
+        nb = self.nblk[sids].astype(np.int64)
+        need_new = pos % B == 0
+        last = np.where(need_new, 0, self.tables[sids, np.maximum(nb - 1, 0)]).astype(np.int64)
+        shared = (~need_new) & (self.ref[last] > 1)
+        cow = np.zeros(len(sids), dtype=bool)
+        ref_after = {}
+        for i in np.flatnonzero(shared):          # rare: seqs on a shared partial block
+            b = int(last[i])
+            c = ref_after.get(b, int(self.ref[b]))
+            if c > 1:
+                cow[i] = True
+                ref_after[b] = c - 1
+        takers = need_new | cow
+        k = int(takers.sum())
+        if k > len(self._free):
+            raise OutOfBlocks(f"need {k} blocks, {len(self._free)} free")
+        if (nb[need_new] + 1 > self.max_blocks_per_seq).any():
+            raise ValueError("sequence would exceed max_blocks_per_seq")
+        fresh = self._take(k)
+        idx = np.flatnonzero(takers)
+        got = np.empty(len(sids), dtype=np.int64)
+        got[idx] = fresh
+        for b, c in ref_after.items():
+            self.ref[b] = c
+        nn = np.flatnonzero(need_new)
+        self.tables[sids[nn], nb[nn]] = got[nn]
+        self.nblk[sids[nn]] += 1
+        cw = np.flatnonzero(cow)
+        self.tables[sids[cw], nb[cw] - 1] = got[cw]
+        pairs = np.stack([last[cw], got[cw]], axis=1).astype(np.int32)
+        slots = self.tables[sids, pos // B].astype(np.int64) * B + pos % B
+        self.lens[sids] += 1
+        return slots.astype(np.int32), pairs
+
+    def fork(self, sid: int, n: int = 1):
+        """``n`` new sequences sharing every block of ``sid`` by reference."""
+        self._check(sid)
+        if n > len(self._rows):
+            raise RuntimeError("no free sequence row (max_seqs reached)")
+        nb = int(self.nblk[sid])
+        out = []
+        for _ in range(n):
+            c = self.new_seq()
+            self.tables[c] = self.tables[sid]
+            self.lens[c] = self.lens[sid]
+            self.nblk[c] = nb
+            self.ref[self.tables[sid, :nb]] += 1
+            out.append(c)
+        return out
+
+    def free(self, sid: int) -> None:
+        """Drop the sequence; blocks whose count reaches zero return to the
+        back of the free list in logical order."""
+        self._check(sid)
+        nb = int(self.nblk[sid])
+        blocks = self.tables[sid, :nb].copy()
+        self.ref[blocks] -= 1
+        for b in blocks[self.ref[blocks] == 0]:
+            self._free.append(int(b))
+        self.tables[sid] = -1
+        self.lens[sid] = 0
+        self.nblk[sid] = 0
+        self.live[sid] = False
+        self._rows.append(sid)
+
+    # --------------------------------------------------------------- queries
+    def context_len(self, sid: int) -> int:
+        return int(self.lens[sid])
+
+    def block_table(self, sid: int) -> np.ndarray:
+        return self.tables[sid, :self.nblk[sid]].copy()
+
+    def waste(self, sid: int) -> int:
+        """Idle slots of the sequence (all in its last block)."""
+        return int(self.nblk[sid]) * self.block_size - int(self.lens[sid])
+
+    def validate(self) -> None:
+        """Check every invariant; raises AssertionError on the first breach."""
+        count = np.zeros(self.num_blocks, dtype=np.int64)
+        for sid in np.flatnonzero(self.live):
+            nb = int(self.nblk[sid])
+            row = self.tables[sid, :nb]
+            assert nb == -(-int(self.lens[sid]) // self.block_size), "block count"
+            assert (self.tables[sid, nb:] == -1).all(), "table padding"
+            assert len(np.unique(row)) == nb, "block repeated within a sequence"
+            assert 0 <= self.waste(sid) < self.block_size or nb == 0, "waste bound"
+            count[row] += 1
+        assert (count == self.ref).all(), "refcount != number of references"
+        free = np.fromiter(self._free, dtype=np.int64, count=len(self._free))
+        assert len(np.unique(free)) == len(free), "block twice on the free list"
+        assert (self.ref[free] == 0).all(), "referenced block on the free list"
+        assert len(free) + int((self.ref > 0).sum()) == self.num_blocks, "block leaked"
