@@ -1,0 +1,216 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: paged KV-cache attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method: every sequence's KV cache is cut into fixed-size blocks of
+ * block_size tokens; a per-sequence block table maps logical block i to a
+ * physical block id in one global pool, and the attention kernels reach keys
+ * and values by following that table ("Paged Attention for Efficient Memory
+ * Management", The Daily Triptych: "At a glance", technical summary, "Look
+ * closer / Logical blocks, physical frames"; "PagedAttention and
+ * RadixAttention: Let's Talk About KV Cache", section "PagedAttention: Memory
+ * Like an Operating System").  The block manager that decides which block a
+ * token goes to lives on the host; these calls are the device side.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor arguments are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing, frees nothing and never synchronises.
+ *  - Every call is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns once the work is enqueued.
+ *  - Return value: PKV_OK (0) or a negative PKV_ERR_* code; on error nothing
+ *    was enqueued and paged_kv_last_error() describes the problem (a
+ *    per-thread string, valid until the next call on that thread).
+ *  - dtype: PKV_DTYPE_FP32 (IEEE binary32) or PKV_DTYPE_BF16 (bfloat16).
+ *    Every floating-point tensor of one call has that dtype, except the
+ *    decode workspace (fp32).
+ *  - block_size: 16 (the pages' default, "PagedAttention 与 RadixAttention",
+ *    section "PagedAttention").  head_dim: 64 or 128.  num_q_heads must be
+ *    a multiple of num_kv_heads with a group of at most 16 query heads per
+ *    KV head (query head j uses KV head j / (num_q_heads / num_kv_heads)).
+ *  - Device memory is addressed with 64-bit offsets: pools of any size.
+ *
+ * Pool layout (both pools hold num_blocks blocks; e = element):
+ *    k_pool  [num_blocks][num_kv_heads][block_size][head_dim]
+ *            -- a key vector is one contiguous row.
+ *    v_pool  [num_blocks][num_kv_heads][head_dim][block_size]
+ *            -- values are stored transposed inside a block: one row of
+ *               block_size tokens per channel.
+ *  A slot is phys_block * block_size + offset_in_block.
+ *
+ * Safety: kernels never touch memory outside the ranges the arguments
+ * describe.  Table entries or slots outside [0, num_blocks) are skipped
+ * (append, copy) or read as block 0 (attention); results are then
+ * unspecified but no out-of-range access happens.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK              0
+#define PKV_ERR_INVALID    -1  /* null pointer, bad size, bad head ratio      */
+#define PKV_ERR_UNSUPPORTED -2 /* dtype / head_dim / block_size / group size  */
+#define PKV_ERR_WORKSPACE  -3  /* decode workspace missing or too small       */
+#define PKV_ERR_LAUNCH     -4  /* the HIP runtime refused a kernel launch     */
+
+#define PKV_DTYPE_FP32 0
+#define PKV_DTYPE_BF16 1
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* paged_kv_last_error(void);
+
+/*
+ * paged_kv_append -- write new tokens' keys and values into their pool slots.
+ *
+ * Passage: a new token's keys and values go into the next slot of the
+ * sequence's current block, a fresh block being taken when the current one
+ * is full (Triptych page, technical summary and "The story").  The host
+ * allocator chooses the slots; this call only writes.
+ *
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim]   (dtype)
+ *   slot_mapping   [num_tokens] int32; slot < 0 = skip the token
+ *   k_pool, v_pool pools as laid out above (written in place)
+ *
+ * Every head of token t goes to slot_mapping[t].  Slots within one call must
+ * be distinct (else which write wins is unspecified).  num_tokens == 0 is a
+ * no-op.  Result is a bit copy: no value changes.
+ */
+int paged_kv_append(const void* k_new, const void* v_new,
+                    const int32_t* slot_mapping, int32_t num_tokens,
+                    void* k_pool, void* v_pool, int32_t num_blocks,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t dtype, void* stream);
+
+/*
+ * copy_blocks -- copy-on-write of shared blocks.
+ *
+ * Passage: once a forked sequence writes into a block other sequences still
+ * reference, that block is copied first so the other references keep their
+ * contents (Triptych page, technical summary, "Look closer / Sharing is a
+ * pointer change" and "The story").
+ *
+ *   block_mapping  [num_pairs][2] int32 (src, dst), device memory
+ *
+ * For every pair the whole K block and the whole V block (all heads, all
+ * block_size slots) of src are copied to dst, bit for bit.  Destinations must
+ * be distinct and no destination may also be a source of the same call (the
+ * result is then independent of pair order).  num_pairs == 0 is a no-op.
+ */
+int copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks,
+                const int32_t* block_mapping, int32_t num_pairs,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t dtype, void* stream);
+
+/*
+ * Size in bytes of the fp32 workspace paged_attention_decode needs for these
+ * arguments (0 when every context fits one partition).  partition_size as in
+ * paged_attention_decode (0 = the library's choice).  Returns 0 for invalid
+ * arguments as well; the decode call reports those.
+ */
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_context_len,
+                                             int32_t partition_size);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends to its
+ * whole paged context.
+ *
+ * Passage: the attention kernel walks the block table and gathers the
+ * sequence's physical blocks; the result equals attention over the same
+ * tokens stored contiguously (Triptych page, technical summary, "The story",
+ * "The surprising detail").  Long contexts are split into partitions along
+ * the sequence that run in parallel and are merged afterwards ("RadixAttention:
+ * Tree-Based KV Cache Reuse in SGLang Guide", section "3. Integrating
+ * FlashInfer for Sub-Millisecond Paged Kernel Lookups", split-KV decode).
+ *
+ *   out            [num_seqs][num_q_heads][head_dim]  (dtype), written
+ *   q              [num_seqs][num_q_heads][head_dim]  (dtype)
+ *   block_tables   [num_seqs][max_blocks_per_seq] int32; row s, entries
+ *                  0 .. ceil(context_lens[s]/block_size)-1 are read
+ *   context_lens   [num_seqs] int32, tokens in each context (the decoded
+ *                  token's own key/value included); 0 gives a zero row
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid;
+ *                  contexts longer than it are cut to it)
+ *   scale          softmax scale applied to q.k
+ *   partition_size tokens per split-KV partition, a multiple of block_size,
+ *                  or 0 for the library's choice
+ *   workspace      fp32 scratch of at least
+ *                  paged_attention_decode_workspace_size(...) bytes (may be
+ *                  NULL when that size is 0).  Layout, P = number of
+ *                  partitions of max_context_len:
+ *                    o_part [num_seqs][num_q_heads][P][head_dim]
+ *                    m_part [num_seqs][num_q_heads][P]  max scaled score
+ *                    l_part [num_seqs][num_q_heads][P]  sum exp(score - m)
+ *                  where o_part is the partition's normalised output.
+ *
+ * out[s][j] = sum_t softmax_t(scale * q[s][j] . k_t) v_t over t < context_lens[s],
+ * with k_t, v_t from KV head j / (num_q_heads/num_kv_heads).  Arithmetic:
+ * fp32 accumulation (bf16 products on the matrix cores for bf16 input).
+ */
+int paged_attention_decode(void* out, const void* q,
+                           const void* k_pool, const void* v_pool, int32_t num_blocks,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           float scale, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t dtype, void* stream);
+
+/*
+ * paged_attention_extend -- new tokens of each request (a chunked prefill
+ * after a cached prefix) attend causally to the prefix plus themselves.
+ *
+ * Passage: with the prefix's keys and values already in the pool, only the
+ * unseen suffix is computed ("RadixAttention: Tree-Based KV Cache Reuse in
+ * SGLang Guide", "RadixAttention Architecture", longest-prefix search and
+ * prefill bypass; "PagedAttention and RadixAttention: Let's Talk About KV
+ * Cache", section "RadixAttention: A Tree That Does Not Forget").  Prefill
+ * is the compute-bound phase (same guide, "1. The Quadratic Cost ...").
+ *
+ *   out, q         [total_q][num_q_heads][head_dim]  (dtype)
+ *   cu_seqlens_q   [num_reqs+1] int32: request r owns rows cu[r] .. cu[r+1]-1
+ *   seq_lens       [num_reqs] int32: prefix + new tokens of request r; the
+ *                  new tokens' keys/values must already be in the pool
+ *   max_q_len      host-side bound of cu[r+1]-cu[r]   (sizes the grid)
+ *   max_seq_len    host-side bound of seq_lens         (informational)
+ *   block_tables   [num_reqs][max_blocks_per_seq] int32
+ *
+ * New token i of request r (position P_r + i, P_r = seq_lens[r] - n_r)
+ * attends to positions 0 .. P_r + i.  Arithmetic: bf16 matrix-core products
+ * with fp32 accumulation for bf16; fp32 throughout for fp32.
+ */
+int paged_attention_extend(void* out, const void* q,
+                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                           int32_t num_reqs, int32_t total_q, int32_t max_q_len,
+                           int32_t max_seq_len,
+                           const void* k_pool, const void* v_pool, int32_t num_blocks,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, float scale, int32_t dtype, void* stream);
+
+/*
+ * paged_kv_gather -- copy one sequence's keys and values, in logical order,
+ * out of the pool (the kernel-side walk of the block table, exposed so that
+ * tests can check device-side indexing bit for bit).
+ *
+ *   k_out, v_out   [context_len][num_kv_heads][head_dim]  (dtype), written
+ *   block_table_row [ceil(context_len/block_size)] int32, device memory
+ */
+int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                    int32_t num_blocks, const int32_t* block_table_row,
+                    int32_t context_len, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,188 @@
+"""ctypes binding of libpagedkv.so.
+
+Argument marshalling only: shapes and dtypes are checked on the host, raw
+device pointers and torch's current HIP stream are handed to the C ABI, and a
+non-zero status becomes a :class:`PagedKVError`.  Every step runs in the
+library's kernels; there is no other implementation in this module.
+
+Function names and argument meanings follow ``include/pagedkv.h``.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+_LIB = None
+
+PKV_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+SYMBOLS = ("paged_kv_append", "copy_blocks", "paged_attention_decode_workspace_size",
+           "paged_attention_decode", "paged_attention_extend", "paged_kv_gather",
+           "paged_kv_last_error")
+
+
+class PagedKVError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+
+def load():
+    """Load the library once (after torch, so the HIP runtime torch already
+    loaded is the one the library binds to).  Raises if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise PagedKVError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_63_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, p, f32, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.paged_kv_last_error.restype = ctypes.c_char_p
+    lib.paged_kv_last_error.argtypes = []
+    lib.paged_kv_append.restype = ctypes.c_int
+    lib.paged_kv_append.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, p]
+    lib.copy_blocks.restype = ctypes.c_int
+    lib.copy_blocks.argtypes = [p, p, i32, p, i32, i32, i32, i32, i32, p]
+    lib.paged_attention_decode_workspace_size.restype = sz
+    lib.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode.argtypes = [p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32,
+                                           i32, f32, i32, p, sz, i32, p]
+    lib.paged_attention_extend.restype = ctypes.c_int
+    lib.paged_attention_extend.argtypes = [p, p, p, p, i32, i32, i32, i32, p, p, i32, p, i32,
+                                           i32, i32, i32, i32, f32, i32, p]
+    lib.paged_kv_gather.restype = ctypes.c_int
+    lib.paged_kv_gather.argtypes = [p, p, p, p, i32, p, i32, i32, i32, i32, i32, p]
+    _LIB = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise PagedKVError(f"status {rc}: {load().paged_kv_last_error().decode()}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _int32(*ts):
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise ValueError("index tensors must be int32")
+
+
+def _pools(k_pool, v_pool):
+    if k_pool.dim() != 4 or v_pool.dim() != 4:
+        raise ValueError("pools must be 4-D")
+    nb, hkv, bs, d = k_pool.shape
+    if tuple(v_pool.shape) != (nb, hkv, d, bs):
+        raise ValueError(f"v_pool must be [num_blocks][Hkv][D][B] = {(nb, hkv, d, bs)}, "
+                         f"got {tuple(v_pool.shape)}")
+    if k_pool.dtype != v_pool.dtype or k_pool.dtype not in PKV_DTYPE:
+        raise ValueError("pools must share a dtype in (float32, bfloat16)")
+    return nb, hkv, bs, d, PKV_DTYPE[k_pool.dtype]
+
+
+def new_pools(num_blocks, num_kv_heads, head_dim, block_size=16, dtype=torch.bfloat16,
+              device="cuda"):
+    """Empty K and V pools in the library's layout (contents undefined)."""
+    k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+    return k, v
+
+
+def paged_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool):
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    _dev(k_new, v_new, slot_mapping, k_pool, v_pool)
+    _int32(slot_mapping)
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d):
+        raise ValueError("k_new/v_new must be [T][Hkv][D]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new/v_new dtype must match the pools")
+    _check(load().paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T, _ptr(k_pool),
+                                  _ptr(v_pool), nb, hkv, d, bs, dt, _stream()))
+
+
+def copy_blocks(k_pool, v_pool, block_mapping):
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    _dev(k_pool, v_pool, block_mapping)
+    _int32(block_mapping)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [N][2]")
+    _check(load().copy_blocks(_ptr(k_pool), _ptr(v_pool), nb, _ptr(block_mapping),
+                              block_mapping.shape[0], hkv, d, bs, dt, _stream()))
+
+
+def paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          max_context_len, partition_size=0):
+    return int(load().paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                             head_dim, max_context_len,
+                                                             partition_size))
+
+
+def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                           scale, partition_size=0, workspace=None):
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    _dev(out, q, k_pool, v_pool, block_tables, context_lens)
+    _int32(block_tables, context_lens)
+    S, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (S, hq, d) or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("q/out must be [S][Hq][D] in the pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables [S][max_blocks], context_lens [S]")
+    need = paged_attention_decode_workspace_size(S, hq, hkv, d, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev(workspace)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().paged_attention_decode(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb,
+                                         _ptr(block_tables), block_tables.shape[1],
+                                         _ptr(context_lens), S, int(max_context_len), hq, hkv, d,
+                                         bs, float(scale), int(partition_size), _ptr(workspace),
+                                         wbytes, dt, _stream()))
+    return workspace
+
+
+def paged_attention_extend(out, q, cu_seqlens_q, seq_lens, k_pool, v_pool, block_tables,
+                           max_q_len, max_seq_len, scale):
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    _dev(out, q, cu_seqlens_q, seq_lens, k_pool, v_pool, block_tables)
+    _int32(cu_seqlens_q, seq_lens, block_tables)
+    Tq, hq, dq = q.shape
+    R = seq_lens.shape[0]
+    if dq != d or tuple(out.shape) != (Tq, hq, d) or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("q/out must be [Tq][Hq][D] in the pool dtype")
+    if cu_seqlens_q.shape[0] != R + 1 or block_tables.dim() != 2 or block_tables.shape[0] != R:
+        raise ValueError("cu_seqlens_q [R+1], seq_lens [R], block_tables [R][max_blocks]")
+    _check(load().paged_attention_extend(_ptr(out), _ptr(q), _ptr(cu_seqlens_q), _ptr(seq_lens),
+                                         R, Tq, int(max_q_len), int(max_seq_len), _ptr(k_pool),
+                                         _ptr(v_pool), nb, _ptr(block_tables),
+                                         block_tables.shape[1], hq, hkv, d, bs, float(scale), dt,
+                                         _stream()))
+
+
+def paged_kv_gather(k_out, v_out, k_pool, v_pool, block_table_row, context_len):
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    _dev(k_out, v_out, k_pool, v_pool, block_table_row)
+    _int32(block_table_row)
+    if tuple(k_out.shape) != (context_len, hkv, d) or tuple(v_out.shape) != (context_len, hkv, d):
+        raise ValueError("k_out/v_out must be [context_len][Hkv][D]")
+    _check(load().paged_kv_gather(_ptr(k_out), _ptr(v_out), _ptr(k_pool), _ptr(v_pool), nb,
+                                  _ptr(block_table_row), int(context_len), hkv, d, bs, dt,
+                                  _stream()))

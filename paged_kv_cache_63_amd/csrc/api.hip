@@ -1,0 +1,219 @@
+// C-ABI entry points: argument checks, workspace sizing and dispatch to the
+// kernel launchers.  Nothing here allocates or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/pagedkv.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return PKV_OK;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_DTYPE_FP32 ? 4 : dtype == PKV_DTYPE_BF16 ? 2 : 0; }
+
+// Shared shape checks; returns PKV_OK or an error code (message set).
+int check_common(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype) {
+  if (!elem_bytes(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported (0=fp32, 1=bf16)", dtype);
+  if (block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "block_size %d not supported (16)", block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
+  if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "num_kv_heads must be positive");
+  return PKV_OK;
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(PKV_ERR_INVALID, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "query heads per KV head %d > 16", num_q_heads / num_kv_heads);
+  return PKV_OK;
+}
+
+constexpr int32_t kMaxPartitionTokens = 4096;  // 256 blocks: one table entry per lane of a wave
+constexpr int32_t kMaxPartitions = 16384;      // LDS weights of the merge pass
+
+int32_t choose_partition(int32_t partition_size) {
+  return partition_size > 0 ? partition_size : 512;
+}
+
+int32_t num_partitions(int32_t max_context_len, int32_t ptok) {
+  return max_context_len <= 0 ? 1 : (max_context_len + ptok - 1) / ptok;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* paged_kv_last_error(void) { return g_err; }
+
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                    int32_t num_tokens, void* k_pool, void* v_pool, int32_t num_blocks,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                    void* stream) {
+  int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
+  if (rc) return rc;
+  if (num_tokens < 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID, "bad num_tokens/num_blocks");
+  if (num_tokens == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if ((int64_t)num_blocks * block_size > INT32_MAX)
+    return fail(PKV_ERR_INVALID, "num_blocks * block_size exceeds the int32 slot range");
+  rc = pkv::launch_append(k_new, v_new, slot_mapping, num_tokens, k_pool, v_pool, num_blocks,
+                          num_kv_heads, head_dim, block_size, elem_bytes(dtype), (hipStream_t)stream);
+  return rc ? fail(rc, "append launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();
+}
+
+int copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, const int32_t* block_mapping,
+                int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t dtype, void* stream) {
+  int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
+  if (rc) return rc;
+  if (num_pairs < 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID, "bad num_pairs/num_blocks");
+  if (num_pairs == 0) return ok();
+  if (num_pairs > 65535) return fail(PKV_ERR_INVALID, "num_pairs %d > 65535 per call", num_pairs);
+  if (!k_pool || !v_pool || !block_mapping) return fail(PKV_ERR_INVALID, "null pointer argument");
+  rc = pkv::launch_copy_blocks(k_pool, v_pool, num_blocks, block_mapping, num_pairs, num_kv_heads,
+                               head_dim, block_size, elem_bytes(dtype), (hipStream_t)stream);
+  return rc ? fail(rc, "copy_blocks launch failed") : ok();
+}
+
+int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                    int32_t num_blocks, const int32_t* block_table_row, int32_t context_len,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                    void* stream) {
+  int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
+  if (rc) return rc;
+  if (context_len < 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID, "bad context_len/num_blocks");
+  if (context_len == 0) return ok();
+  if (!k_out || !v_out || !k_pool || !v_pool || !block_table_row)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  rc = pkv::launch_gather(k_out, v_out, k_pool, v_pool, num_blocks, block_table_row, context_len,
+                          num_kv_heads, head_dim, block_size, elem_bytes(dtype), (hipStream_t)stream);
+  return rc ? fail(rc, "gather launch failed") : ok();
+}
+
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_context_len, int32_t partition_size) {
+  (void)num_kv_heads;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  const int32_t ptok = choose_partition(partition_size);
+  if (ptok <= 0) return 0;
+  const int64_t P = num_partitions(max_context_len, ptok);
+  if (P <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
+}
+
+int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           int32_t num_blocks, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           int32_t dtype, void* stream) {
+  int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
+  if (rc) return rc;
+  rc = check_heads(num_q_heads, num_kv_heads);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID, "bad num_seqs/num_blocks/max_blocks_per_seq/max_context_len");
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if ((int64_t)num_seqs * num_kv_heads > INT32_MAX) return fail(PKV_ERR_INVALID, "too many sequences");
+  const int32_t ptok = choose_partition(partition_size);
+  if (ptok % block_size || ptok > kMaxPartitionTokens)
+    return fail(PKV_ERR_INVALID, "partition_size %d must be a multiple of %d and <= %d",
+                partition_size, block_size, kMaxPartitionTokens);
+  const int32_t P = num_partitions(max_context_len, ptok);
+  if (P > kMaxPartitions || P > 65535)
+    return fail(PKV_ERR_INVALID, "max_context_len %d needs %d partitions (> %d)", max_context_len, P,
+                kMaxPartitions);
+  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                            head_dim, max_context_len, ptok);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  if (P > 1) {
+    float* ws = (float*)workspace;
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * P;
+    a.part_o = ws;
+    a.part_m = ws + rows * head_dim;
+    a.part_l = a.part_m + rows;
+  }
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.partition_blocks = ptok / block_size;
+  a.max_partitions = P;
+  a.scale = scale;
+  rc = pkv::launch_decode(a, dtype, (hipStream_t)stream);
+  return rc ? fail(rc, "decode launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();
+}
+
+int paged_attention_extend(void* out, const void* q, const int32_t* cu_seqlens_q,
+                           const int32_t* seq_lens, int32_t num_reqs, int32_t total_q,
+                           int32_t max_q_len, int32_t max_seq_len, const void* k_pool,
+                           const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                           void* stream) {
+  int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
+  if (rc) return rc;
+  rc = check_heads(num_q_heads, num_kv_heads);
+  if (rc) return rc;
+  if (num_reqs < 0 || total_q < 0 || max_q_len < 0 || max_seq_len < 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID, "negative size argument");
+  if (num_reqs == 0 || total_q == 0) return ok();
+  if (!out || !q || !cu_seqlens_q || !seq_lens || !k_pool || !v_pool || !block_tables)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (max_q_len > 65535 && dtype == PKV_DTYPE_FP32)
+    return fail(PKV_ERR_INVALID, "max_q_len %d > 65535 for fp32", max_q_len);
+  pkv::ExtendArgs a{};
+  a.out = out;
+  a.q = q;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens = seq_lens;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.num_reqs = num_reqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  rc = pkv::launch_extend(a, dtype, (hipStream_t)stream);
+  return rc ? fail(rc, "extend launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();
+}
+
+}  // extern "C"

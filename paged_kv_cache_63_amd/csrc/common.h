@@ -1,0 +1,91 @@
+// Internal helpers shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// ---- vector types for the matrix-core builtins and wide memory accesses ----
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// bf16 word -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t w) { return __uint_as_float((uint32_t)w << 16); }
+
+// fp32 -> bf16 word, round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+}  // namespace pkv
+
+// ---- C++ launchers implemented in the kernel translation units ----
+// Each returns 0 on success or a PKV_ERR_* code; arguments are already
+// validated by the C-ABI layer.
+namespace pkv {
+
+int launch_append(const void* k_new, const void* v_new, const int32_t* slots, int32_t num_tokens,
+                  void* k_pool, void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d,
+                  int32_t bs, int32_t elem_bytes, hipStream_t st);
+
+int launch_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, const int32_t* mapping,
+                       int32_t num_pairs, int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
+                       hipStream_t st);
+
+int launch_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                  int32_t num_blocks, const int32_t* row, int32_t ctx, int32_t hkv, int32_t d,
+                  int32_t bs, int32_t elem_bytes, hipStream_t st);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_o;   // [S][Hq][P][D]
+  float* part_m;   // [S][Hq][P]
+  float* part_l;   // [S][Hq][P]
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t partition_blocks;  // blocks per split-KV partition
+  int32_t max_partitions;    // P
+  float scale;
+};
+
+int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st);
+
+struct ExtendArgs {
+  void* out;
+  const void* q;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seq_lens;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  int32_t num_reqs;
+  int32_t total_q;
+  int32_t max_q_len;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float scale;
+};
+
+int launch_extend(const ExtendArgs& a, int32_t dtype, hipStream_t st);
+
+}  // namespace pkv

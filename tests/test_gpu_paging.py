@@ -1,0 +1,125 @@
+"""Bit-exact parity of the pool-moving calls (append, copy_blocks, gather)
+and of the allocator's slots/tables against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_pins as P
+from gpu_helpers import LibDecodeState, i32, poisoned_pools, to_dev, words_of
+from oracle import block_manager, paging
+from paged_kv_cache_63_amd import BlockAllocator, _lib
+from workloads import decode_case, gqa4_decode, normal_words, tiny_fp32_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_slots_tables(case):
+    bm = block_manager.RefBlockManager(case.num_blocks, 16, case.free_order)
+    slots, tables = [], []
+    for L in case.context_lens:
+        sid = bm.new_seq()
+        s, _ = bm.append(sid, int(L))
+        slots += s
+        tables.append(bm.table(sid))
+    return np.asarray(slots), tables
+
+
+@pytest.mark.parametrize("case_fn", [
+    lambda: tiny_fp32_decode(),
+    lambda: decode_case(101, 7, 1, 300, 8, 2, 128, "bf16", spare_blocks=5),
+    lambda: decode_case(102, 5, 1, 200, 4, 4, 64, "bf16"),
+    lambda: decode_case(103, 5, 1, 200, 6, 3, 128, "fp32"),
+], ids=["tiny-fp32", "bf16-d128", "bf16-d64", "fp32-d128"])
+def test_append_pool_bit_exact(gpu, case_fn):
+    case = case_fn()
+    st = LibDecodeState(case)
+    slots, tables = _oracle_slots_tables(case)
+    assert np.array_equal(st.slots, slots)                      # a1: slots
+    for s, t in enumerate(tables):                              # a1: tables
+        row = st.alloc.tables[s]
+        assert row[:len(t)].tolist() == t and (row[len(t):] == -1).all()
+    kp, vp = paging.new_pools(case.num_blocks, case.num_kv_heads, case.head_dim, 16, case.dtype)
+    paging.append(kp, vp, case.k, case.v, slots, 16)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_of(st.k_pool), kp)              # a2: whole pool, NaN included
+    assert np.array_equal(words_of(st.v_pool), vp)
+
+
+def test_append_full_size_gqa4(gpu):
+    """Llama-3-8B-shaped pool (64 sequences, ~147K tokens, 0.6 GB): every word."""
+    case = gqa4_decode()
+    st = LibDecodeState(case)
+    kp, vp, _ = P.oracle_pools_for_decode(case)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_of(st.k_pool), kp)
+    assert np.array_equal(words_of(st.v_pool), vp)
+
+
+def test_append_skips_negative_slots(gpu):
+    k, v = poisoned_pools(4, 2, 64, "bf16")
+    before = words_of(k).copy()
+    kn = torch.ones((3, 2, 64), dtype=torch.bfloat16, device="cuda")
+    _lib.paged_kv_append(kn, kn, i32([-1, 21, -7]), k, v)     # slot 21 = block 1, offset 5
+    after = words_of(k)
+    assert (after[1, :, 5, :] == 0x3F80).all()                  # bf16 1.0
+    after[1, :, 5, :] = before[1, :, 5, :]
+    assert np.array_equal(after, before)                        # nothing else written
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_copy_blocks_bit_exact(gpu, dtype, d):
+    rng = np.random.default_rng(7)
+    nb, hkv = 40, 8
+    kw = normal_words(rng, (nb, hkv, 16, d), dtype)
+    vw = normal_words(rng, (nb, hkv, d, 16), dtype)
+    pairs = np.array([[3, 30], [17, 2], [5, 39], [0, 12]])
+    k, v = to_dev(kw, dtype), to_dev(vw, dtype)
+    _lib.copy_blocks(k, v, i32(pairs))
+    kr, vr = kw.copy(), vw.copy()
+    paging.copy_blocks(kr, vr, pairs)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_of(k), kr) and np.array_equal(words_of(v), vr)
+
+
+@pytest.mark.parametrize("case_fn", [
+    lambda: decode_case(111, 3, 1, 500, 8, 2, 128, "bf16"),
+    lambda: decode_case(112, 3, 1, 100, 4, 4, 64, "fp32"),
+], ids=["bf16", "fp32"])
+def test_gather_bit_exact(gpu, case_fn):
+    case = case_fn()
+    st = LibDecodeState(case)
+    kp, vp, tab = P.oracle_pools_for_decode(case)
+    for s in range(case.num_seqs):
+        L = int(case.context_lens[s])
+        ko = torch.empty((L, case.num_kv_heads, case.head_dim), dtype=st.q.dtype, device="cuda")
+        vo = torch.empty_like(ko)
+        _lib.paged_kv_gather(ko, vo, st.k_pool, st.v_pool, st.tables[s].contiguous(), L)
+        kr, vr = paging.gather(kp, vp, tab[s], L, 16)
+        assert np.array_equal(words_of(ko), kr) and np.array_equal(words_of(vo), vr)
+        c0, c1 = case.cu_tokens[s], case.cu_tokens[s + 1]
+        assert np.array_equal(kr, case.k[c0:c1])
+
+
+def test_decode_step_allocator_and_append(gpu):
+    """Steps of one-token appends (allocate on overflow) through the batched
+    allocator path, compared with the oracle model and oracle append."""
+    rng = np.random.default_rng(5)
+    S, hkv, d, nb = 12, 2, 64, 400
+    order = rng.permutation(nb)
+    lib = BlockAllocator(nb, 16, max_seqs=S, max_blocks_per_seq=40, free_order=order)
+    ref = block_manager.RefBlockManager(nb, 16, order)
+    sids = [lib.new_seq() for _ in range(S)]
+    rids = [ref.new_seq() for _ in range(S)]
+    k, v = poisoned_pools(nb, hkv, d, "bf16")
+    kr, vr = paging.new_pools(nb, hkv, d, 16, "bf16")
+    for step in range(40):
+        kw = normal_words(rng, (S, hkv, d), "bf16")
+        vw = normal_words(rng, (S, hkv, d), "bf16")
+        slots, pairs = lib.append_step(sids)
+        want = [ref.append(r, 1)[0][0] for r in rids]
+        assert slots.tolist() == want and len(pairs) == 0
+        _lib.paged_kv_append(to_dev(kw, "bf16"), to_dev(vw, "bf16"), i32(slots), k, v)
+        paging.append(kr, vr, kw, vw, np.asarray(want), 16)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_of(k), kr) and np.array_equal(words_of(v), vr)

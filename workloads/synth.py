@@ -1,8 +1,10 @@
 """Seeded input generators (random draws and shapes only).
 
-Values: keys, values and queries are standard normal draws in float32
-(``rng.standard_normal(dtype=float32)``); bf16 inputs are those draws rounded
-to nearest-even bfloat16.  Integer lengths are inclusive uniform draws
+Values: keys, values and queries are standard normal draws in float32,
+made by the Box-Muller transform of float32 uniforms; a tensor is filled in
+fixed chunks of 2^22 values, chunk i from the i-th child generator spawned
+from the seed's generator (so the bits do not depend on how many threads fill
+it).  bf16 inputs are those draws rounded to nearest-even bfloat16.  Integer lengths are inclusive uniform draws
 (``rng.integers(lo, hi, endpoint=True)``), deliberately not multiples of the
 block size, so partly filled last blocks occur.  The order in which physical
 blocks leave the free list is a seeded permutation of the pool, so the blocks
@@ -17,6 +19,8 @@ KV Cache Reuse in SGLang Guide", "Multi-Candidate Tree Search"), and multi-turn
 prefill over a cached history (same guide, "The Problem").
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -32,14 +36,41 @@ def bf16_words(x: np.ndarray) -> np.ndarray:
     return ((bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
 
 
+_CHUNK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _box_muller(rng, n: int) -> np.ndarray:
+    """n standard normal float32 values from 2*ceil(n/2) uniforms."""
+    h = (n + 1) // 2
+    u1 = np.float32(1) - rng.random(h, dtype=np.float32)      # (0, 1]
+    u2 = rng.random(h, dtype=np.float32)
+    r = np.sqrt(np.float32(-2) * np.log(u1))
+    th = np.float32(2 * np.pi) * u2
+    out = np.empty(2 * h, dtype=np.float32)
+    out[:h] = r * np.cos(th)
+    out[h:] = r * np.sin(th)
+    return out[:n]
+
+
 def normal_words(rng, shape, dtype: str) -> np.ndarray:
     """Standard normal draws stored as raw words of ``dtype``."""
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if dtype == "fp32":
-        return x.view(np.uint32)
-    if dtype == "bf16":
-        return bf16_words(x)
-    raise ValueError(dtype)
+    if dtype not in DTYPES:
+        raise ValueError(dtype)
+    n = int(np.prod(shape))
+    word = np.uint32 if dtype == "fp32" else np.uint16
+    out = np.empty(n, dtype=word)
+    kids = rng.spawn(max(1, -(-n // _CHUNK)))
+
+    def fill(i):
+        a, b = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = _box_muller(kids[i], b - a)
+        out[a:b] = x.view(np.uint32) if dtype == "fp32" else bf16_words(x)
+
+    if n:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(len(kids))))
+    return out.reshape(shape)
 
 
 def _scale(head_dim: int) -> float:
