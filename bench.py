@@ -1,0 +1,491 @@
+#!/usr/bin/env python3
+"""Throughput of the paged KV-cache hot path on one MI355X.
+
+Default workload (the headline): decode steps at the Llama-3-8B attention
+shape -- 64 sequences, contexts drawn uniformly from [512, 4096] tokens,
+32 query heads over 8 KV heads, head_dim 128, bf16, 16-token blocks scattered
+through one pool.  One step is the whole path for one new token per
+sequence:
+
+  host   block manager appends a token to every sequence (slots, new blocks,
+         copy-on-write pairs, block tables)  -> one pinned host->device copy
+  device copy_blocks (when the step produced copy-on-write pairs)
+         paged_kv_append (the new token's K/V into its slot)
+         paged_attention_decode (pass 1 + the log-sum-exp merge)
+
+Contexts grow by one token per step, as in a real decode loop.  All inputs
+(queries and new K/V of every step, the populated pool) are in device memory
+before the timed region.  Prints one JSON line.
+
+Other workloads (``--workload``) exist for measurement, not as the headline:
+long-context-decode (8 x 32K..128K tokens, 64/8 heads), shared-prefix-decode
+(256 + 12 forked sequences behind a 4096-token prompt) and multiturn-extend
+(16 requests x (2K..8K cached + 512 new), bf16 matrix cores).
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak
+METRIC = "paged decode HBM GB/s (% of peak) and tokens/s at Llama-3-8B GQA shape"
+
+WORKLOADS = ("gqa4-decode", "long-context-decode", "shared-prefix-decode", "multiturn-extend")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=WORKLOADS, default="gqa4-decode")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB device copy first (counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+def make_case(name, total_steps):
+    import workloads as W
+    if name == "gqa4-decode":
+        return W.gqa4_decode(spare_blocks=64 * (total_steps // 16 + 2))
+    if name == "long-context-decode":
+        # the long-context workload's draws (seed 3), with room for the decode steps
+        return W.decode_case(3, 8, 32768, 131072, 64, 8, 128, "bf16",
+                             spare_blocks=8 * (total_steps // 16 + 2),
+                             name="long-context-decode-8x32K-128K")
+    if name == "shared-prefix-decode":
+        return W.shared_prefix_decode()
+    return W.multiturn_extend()
+
+
+# ------------------------------------------------------------- cpu baseline
+_CPU = {}
+
+
+def _cpu_worker(seqs):
+    from threadpoolctl import threadpool_limits
+    from oracle import attention
+    c = _CPU
+    with threadpool_limits(1):
+        attention.decode(c["q"], c["kp"], c["vp"], c["tab"], c["lens"], c["scale"], 16, "bf16",
+                         seqs=seqs)
+    return len(seqs)
+
+
+def cpu_baseline(case, seconds):
+    """The oracle (numpy float64) on the same decode workload, one process per
+    host core, one BLAS thread each, each taking whole sequences.  Runs before
+    the GPU is touched (the pool of workers is forked)."""
+    import multiprocessing as mp
+
+    from oracle import block_manager, paging
+    bm = block_manager.RefBlockManager(case.num_blocks, 16, case.free_order)
+    kp, vp = paging.new_pools(case.num_blocks, case.num_kv_heads, case.head_dim, 16, case.dtype)
+    tabs = []
+    for s, L in enumerate(case.context_lens):
+        sid = bm.new_seq()
+        sl, _ = bm.append(sid, int(L))
+        a, b = case.cu_tokens[s], case.cu_tokens[s + 1]
+        paging.append(kp, vp, case.k[a:b], case.v[a:b], np.asarray(sl), 16)
+        tabs.append(bm.table(sid))
+    tab = np.full((len(tabs), max(map(len, tabs))), -1, dtype=np.int64)
+    for i, t in enumerate(tabs):
+        tab[i, :len(t)] = t
+    _CPU.update(q=case.q, kp=kp, vp=vp, tab=tab, lens=case.context_lens, scale=case.scale)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    S = case.num_seqs
+    chunks = [list(range(i, S, cores)) for i in range(cores)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            pool.map(_cpu_worker, chunks)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or el / steps * (steps + 1) > 2.5 * seconds:
+                break
+    _CPU.clear()
+    tok_s = steps * S / el
+    kv_bytes = float(np.sum(case.context_lens)) * 2 * case.num_kv_heads * case.head_dim * 2
+    return {"value": round(tok_s, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} full decode step(s) of the same workload ({S} sequences x "
+                      f"{case.num_q_heads} heads, {int(np.sum(case.context_lens))} context "
+                      f"tokens), {el:.1f} s on {cores} processes x 1 BLAS thread",
+            "gbps": round(steps * kv_bytes / el / 1e9, 4)}
+
+
+# ------------------------------------------------------------------ traffic
+def kernel_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "paged_kv_cache_63_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, files):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/*.json),
+    or None when no measurement exists for the current kernel source."""
+    hsh = kernel_hash(files)
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.json"))):
+        try:
+            with open(p) as f:
+                d = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if d.get("workload") == workload and d.get("kernel_source_hash") == hsh:
+            return d.get("hbm_bytes_per_launch"), d
+    return None, None
+
+
+# ---------------------------------------------------------------- GPU steps
+def run_decode(args, case, torch, lib, alloc_cls):
+    """Decode loop over a plain (unshared) decode case."""
+    dev = torch.device("cuda:0")
+    S, hq, hkv, d = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
+    T = args.warmup + args.steps
+    maxb = -(-(int(case.context_lens.max()) + T + 1) // 16)
+    alloc = alloc_cls(case.num_blocks, 16, max_seqs=S, max_blocks_per_seq=maxb,
+                      free_order=case.free_order)
+    sids = [alloc.new_seq() for _ in range(S)]
+    slots = np.concatenate([alloc.append_tokens(s, int(L))[0] for s, L in zip(sids, case.context_lens)])
+
+    def dev_words(w):
+        return torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k_pool, v_pool = lib.new_pools(case.num_blocks, hkv, d, 16, torch.bfloat16, dev)
+    lib.paged_kv_append(dev_words(case.k), dev_words(case.v),
+                        torch.from_numpy(slots).to(dev), k_pool, v_pool)
+    import workloads as W
+    rng = np.random.default_rng(1000 + S)
+    q_steps = dev_words(W.normal_words(rng, (T, S, hq, d), "bf16"))
+    k_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
+    v_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
+    out = torch.empty((S, hq, d), dtype=torch.bfloat16, device=dev)
+    ws_bytes = lib.paged_attention_decode_workspace_size(S, hq, hkv, d, maxb * 16,
+                                                         args.partition_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    # one pinned staging buffer per in-flight step: [slots | lens | tables]
+    n_i32 = 2 * S + S * maxb
+    ring = [torch.empty(n_i32, dtype=torch.int32, pin_memory=True) for _ in range(3)]
+    ring_np = [r.numpy() for r in ring]
+    ring_ev = [torch.cuda.Event() for _ in range(3)]
+    for e in ring_ev:
+        e.record()
+    stage = torch.empty(n_i32, dtype=torch.int32, device=dev)
+    slots_d = stage[:S]
+    lens_d = stage[S:2 * S]
+    tables_d = stage[2 * S:].view(S, maxb)
+    torch.cuda.synchronize()
+
+    kv_per_tok = 2 * hkv * d * 2
+    ev_pairs = []
+    step_bytes = []
+
+    def step(i, timed):
+        sl, pairs = alloc.append_step(sids)                                  # a1
+        r = i % 3
+        ring_ev[r].synchronize()
+        buf = ring_np[r]
+        buf[:S] = sl
+        buf[S:2 * S] = alloc.lens[:S]
+        buf[2 * S:] = alloc.tables[:S].reshape(-1)
+        stage.copy_(ring[r], non_blocking=True)
+        ring_ev[r].record()
+        if len(pairs):                                                       # a3
+            lib.copy_blocks(k_pool, v_pool, torch.from_numpy(pairs).to(dev))
+        lib.paged_kv_append(k_steps[i], v_steps[i], slots_d, k_pool, v_pool)  # a2
+        mcl = int(alloc.lens[:S].max())
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        lib.paged_attention_decode(out, q_steps[i], k_pool, v_pool, tables_d, lens_d, mcl,
+                                   case.scale, args.partition_size, ws)       # a4 + a5
+        if timed:
+            e1.record()
+            ev_pairs.append((e0, e1))
+            ctx = int(alloc.lens[:S].sum())
+            nblk = int(sum(-(-int(x) // 16) for x in alloc.lens[:S]))
+            step_bytes.append(ctx * kv_per_tok + 2 * S * hq * d * 2 + nblk * 4 + S * 4)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, T):
+        step(i, True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
+    alloc.validate()
+    return dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=step_bytes,
+                ctx_mean=float(alloc.lens[:S].mean()))
+
+
+def run_extend(args, case, torch, lib, alloc_cls):
+    """Repeated extend steps: allocate the new chunk (a1), append it (a2),
+    extend (a6), then hand the chunk's blocks back (truncate)."""
+    dev = torch.device("cuda:0")
+    R = len(case.prefix_lens)
+    hq, hkv, d = case.num_q_heads, case.num_kv_heads, case.head_dim
+    maxb = -(-int(case.seq_lens.max()) // 16) + 1
+    alloc = alloc_cls(case.num_blocks + R, 16, max_seqs=R, max_blocks_per_seq=maxb,
+                      free_order=np.concatenate([case.free_order,
+                                                 np.arange(case.num_blocks, case.num_blocks + R)]))
+    sids = [alloc.new_seq() for _ in range(R)]
+
+    def dev_words(w):
+        return torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ps = np.concatenate([alloc.append_tokens(s, int(p))[0] for s, p in zip(sids, case.prefix_lens)])
+    k_pool, v_pool = lib.new_pools(case.num_blocks + R, hkv, d, 16, torch.bfloat16, dev)
+    lib.paged_kv_append(dev_words(case.prefix_k), dev_words(case.prefix_v),
+                        torch.from_numpy(ps).to(dev), k_pool, v_pool)
+    k_new, v_new, q = dev_words(case.new_k), dev_words(case.new_v), dev_words(case.q)
+    out = torch.empty_like(q)
+    cu = torch.from_numpy(case.cu_new.astype(np.int32)).to(dev)
+    seq_lens = torch.from_numpy(case.seq_lens.astype(np.int32)).to(dev)
+    n_new = int(case.new_lens.sum())
+    ring = [torch.empty(n_new + R * maxb, dtype=torch.int32, pin_memory=True) for _ in range(3)]
+    ring_ev = [torch.cuda.Event() for _ in range(3)]
+    for e in ring_ev:
+        e.record()
+    stage = torch.empty(n_new + R * maxb, dtype=torch.int32, device=dev)
+    slots_d, tables_d = stage[:n_new], stage[n_new:].view(R, maxb)
+    T = args.warmup + args.steps
+    flops = 4.0 * d * hq * float(sum(int(n) * int(p) + int(n) * (int(n) + 1) / 2
+                                     for p, n in zip(case.prefix_lens, case.new_lens)))
+    ev_pairs = []
+    torch.cuda.synchronize()
+
+    def step(i, timed):
+        sl = np.concatenate([alloc.append_tokens(s, int(n))[0] for s, n in zip(sids, case.new_lens)])
+        r = i % 3
+        ring_ev[r].synchronize()
+        buf = ring[r].numpy()
+        buf[:n_new] = sl
+        buf[n_new:] = alloc.tables[:R].reshape(-1)
+        stage.copy_(ring[r], non_blocking=True)
+        ring_ev[r].record()
+        lib.paged_kv_append(k_new, v_new, slots_d, k_pool, v_pool)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        lib.paged_attention_extend(out, q, cu, seq_lens, k_pool, v_pool, tables_d,
+                                   int(case.new_lens.max()), int(case.seq_lens.max()), case.scale)
+        if timed:
+            e1.record()
+            ev_pairs.append((e0, e1))
+        for s, p in zip(sids, case.prefix_lens):
+            alloc.truncate(s, int(p))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, T):
+        step(i, True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
+    return dict(elapsed=el, tokens=n_new * args.steps, durs=durs, flops=flops)
+
+
+def run_shared(args, case, torch, lib, alloc_cls):
+    """Fork + copy-on-write + decode steps over the shared-prefix case: the
+    fork and its copy-on-write step happen in warm-up; timed steps decode all
+    268 sequences (the 4096-token prompt's 256 blocks shared by all)."""
+    dev = torch.device("cuda:0")
+    hq, hkv, d = case.num_q_heads, case.num_kv_heads, case.head_dim
+    T = args.warmup + args.steps
+    S = case.num_decoding
+    extra = S * (T // 16 + 2)
+    nb = case.num_blocks + extra
+    order = np.concatenate([case.free_order, np.arange(case.num_blocks, nb)])
+    maxb = -(-(case.prefix_len + int(case.suffix_lens.max()) + T + 1) // 16)
+    alloc = alloc_cls(nb, 16, max_seqs=S + 1, max_blocks_per_seq=maxb, free_order=order)
+
+    def dev_words(w):
+        return torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k_pool, v_pool = lib.new_pools(nb, hkv, d, 16, torch.bfloat16, dev)
+    root = alloc.new_seq()
+    s, _ = alloc.append_tokens(root, case.prefix_len)
+    lib.paged_kv_append(dev_words(case.prefix_k), dev_words(case.prefix_v),
+                        torch.from_numpy(s).to(dev), k_pool, v_pool)
+    sids, sl = [], []
+    for i in range(len(case.suffix_lens)):
+        sid = alloc.fork(root)[0]
+        sl.append(alloc.append_tokens(sid, int(case.suffix_lens[i]))[0])
+        sids.append(sid)
+    lib.paged_kv_append(dev_words(case.suffix_k), dev_words(case.suffix_v),
+                        torch.from_numpy(np.concatenate(sl)).to(dev), k_pool, v_pool)
+    alloc.free(root)
+    order_s = list(sids)
+    for p in case.parents:
+        order_s += alloc.fork(sids[int(p)], case.samples_per_parent - 1)
+    rows = np.asarray(order_s)
+    import workloads as W
+    rng = np.random.default_rng(4000)
+    q_steps = dev_words(W.normal_words(rng, (T, S, hq, d), "bf16"))
+    k_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
+    v_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
+    out = torch.empty((S, hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, lib.paged_attention_decode_workspace_size(S, hq, hkv, d, maxb * 16, 0)),
+                     dtype=torch.uint8, device=dev)
+    ev_pairs, snaps = [], []
+    kv_per_tok = 2 * hkv * d * 2
+    n_pairs = 0
+    for i in range(T):
+        timed = i >= args.warmup
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        slots, pairs = alloc.append_step(order_s)
+        n_pairs += len(pairs)
+        if len(pairs):
+            lib.copy_blocks(k_pool, v_pool, torch.from_numpy(pairs).to(dev))
+        slots_d = torch.from_numpy(slots).to(dev, non_blocking=True)
+        lens = alloc.lens[rows]
+        tables_d = torch.from_numpy(alloc.tables[rows]).to(dev, non_blocking=True)
+        lens_d = torch.from_numpy(lens).to(dev, non_blocking=True)
+        lib.paged_kv_append(k_steps[i], v_steps[i], slots_d, k_pool, v_pool)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        lib.paged_attention_decode(out, q_steps[i], k_pool, v_pool, tables_d, lens_d,
+                                   int(lens.max()), case.scale, 0, ws)
+        if timed:
+            e1.record()
+            ev_pairs.append((e0, e1))
+            snaps.append((alloc.tables[rows].copy(), lens.copy()))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    uniq, logical = [], []
+    for tabs, lens in snaps:        # distinct (block, used slot) pairs, counted once
+        used = {}
+        for row, L in zip(tabs, lens):
+            nb = -(-int(L) // 16)
+            for j in range(nb):
+                b = int(row[j])
+                used[b] = max(used.get(b, 0), min(16, int(L) - 16 * j))
+        uniq.append(sum(used.values()) * kv_per_tok)
+        logical.append(int(lens.sum()) * kv_per_tok)
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
+    return dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=uniq, logical=logical,
+                cow_pairs=n_pairs)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    T = args.warmup + args.steps
+    if args.workload == "long-context-decode" and args.partition_size == 0:
+        args.partition_size = 512          # the long-context workload's stated split
+    case = make_case(args.workload, T)
+    cpu = None
+    if not args.no_cpu_baseline and args.workload in ("gqa4-decode",):
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    import torch
+    from paged_kv_cache_63_amd import BlockAllocator
+    from paged_kv_cache_63_amd import _lib as lib
+    lib.load()
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+
+    if args.copy_probe:   # a plain copy of known size, for counter calibration
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    if args.workload == "multiturn-extend":
+        r = run_extend(args, case, torch, lib, BlockAllocator)
+        kern = ["extend.hip"]
+    elif args.workload == "shared-prefix-decode":
+        r = run_shared(args, case, torch, lib, BlockAllocator)
+        kern = ["decode.hip"]
+    else:
+        r = run_decode(args, case, torch, lib, BlockAllocator)
+        kern = ["decode.hip"]
+
+    el = r["elapsed"]
+    ms_step = el / args.steps * 1e3
+    mean_dur = float(np.mean(r["durs"]))
+    traffic, _ = load_traffic(args.workload, kern)
+    if args.workload == "multiturn-extend":
+        achieved = r["flops"] / mean_dur / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "paged_attention_extend (extend_bf16_kernel)",
+                "launch_us": round(mean_dur * 1e6, 2), "flops_per_launch": r["flops"]}
+        value = r["tokens"] / el
+        unit = "tokens/s"
+        metric = "paged extend bf16 matrix-core TFLOP/s and new tokens/s (multi-turn prefill)"
+    else:
+        per_launch = float(np.mean(r["bytes"]))
+        achieved = per_launch / mean_dur / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "paged_attention_decode (pass 1 decode_bf16_kernel + pass 2 merge)",
+                "launch_us": round(mean_dur * 1e6, 2), "bytes_per_launch": int(per_launch)}
+        value = r["tokens"] / el
+        unit = "tokens/s"
+        metric = METRIC
+    cfg = {"gqa4-decode": {"workload": "gqa4-decode", "seqs": 64, "context": "U[512,4096] + steps",
+                           "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16,
+                           "layers": 1},
+           "long-context-decode": {"workload": "long-context-decode", "seqs": 8,
+                                   "context": "U[32768,131072] + steps", "q_heads": 64,
+                                   "kv_heads": 8, "head_dim": 128, "block_size": 16,
+                                   "partition_tokens": 512, "layers": 1},
+           "shared-prefix-decode": {"workload": "shared-prefix-decode", "seqs": 268,
+                                    "shared_prefix_tokens": 4096, "suffix": "U[64,1024] + steps",
+                                    "forks": "4 x 4 samples", "q_heads": 32, "kv_heads": 8,
+                                    "head_dim": 128, "block_size": 16, "layers": 1},
+           "multiturn-extend": {"workload": "multiturn-extend", "requests": 16,
+                                "cached_prefix": "U[2048,8192]", "new_tokens": 512,
+                                "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16,
+                                "layers": 1}}[args.workload]
+    if "ctx_mean" in r:
+        cfg["mean_context_in_timed_steps"] = round(r["ctx_mean"] - args.steps / 2, 1)
+    line = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16 K/V/Q, shuffled block placement)",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    if args.workload != "multiturn-extend":
+        line["step_hbm_gbps"] = round(float(np.sum(r["bytes"])) / el / 1e9, 1)
+    if "logical" in r:
+        roof["logical_gbps_effective"] = round(float(np.mean(r["logical"])) / mean_dur / 1e9, 1)
+        line["cow_pairs_in_run"] = r["cow_pairs"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

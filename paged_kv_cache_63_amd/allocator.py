@@ -195,6 +195,23 @@ class BlockAllocator:
             out.append(c)
         return out
 
+    def truncate(self, sid: int, new_len: int) -> None:
+        """Drop the sequence's tokens from ``new_len`` on (a rejected draft, a
+        re-run chunk).  Blocks no longer needed lose this sequence's reference
+        and, at zero, return to the back of the free list in logical order."""
+        self._check(sid)
+        if not 0 <= new_len <= int(self.lens[sid]):
+            raise ValueError("new_len must be within the current length")
+        nb = int(self.nblk[sid])
+        keep = -(-new_len // self.block_size)
+        blocks = self.tables[sid, keep:nb].copy()
+        self.ref[blocks] -= 1
+        for b in blocks[self.ref[blocks] == 0]:
+            self._free.append(int(b))
+        self.tables[sid, keep:nb] = -1
+        self.nblk[sid] = keep
+        self.lens[sid] = new_len
+
     def free(self, sid: int) -> None:
         """Drop the sequence; blocks whose count reaches zero return to the
         back of the free list in logical order."""

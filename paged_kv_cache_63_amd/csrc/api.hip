@@ -45,10 +45,19 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 }
 
 constexpr int32_t kMaxPartitionTokens = 4096;  // 256 blocks: one table entry per lane of a wave
-constexpr int32_t kMaxPartitions = 16384;      // LDS weights of the merge pass
+constexpr int32_t kMaxPartitions = 16384;      // partitions per sequence (grid y)
 
-int32_t choose_partition(int32_t partition_size) {
-  return partition_size > 0 ? partition_size : 512;
+// Library's partition choice: the largest of 1024 / 512 / 256 tokens that
+// still gives at least 1024 (sequence, KV head, partition) work items, so
+// every compute unit gets several; long partitions amortise each
+// workgroup's start-up (table and first K/V fetch).
+int32_t choose_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
+                         int32_t max_context_len) {
+  if (partition_size > 0) return partition_size;
+  const int64_t pairs = (int64_t)num_seqs * (num_kv_heads > 0 ? num_kv_heads : 1);
+  for (int32_t t = 1024; t > 256; t /= 2)
+    if (pairs * ((max_context_len + t - 1) / t) >= 1024) return t;
+  return 256;
 }
 
 int32_t num_partitions(int32_t max_context_len, int32_t ptok) {
@@ -110,9 +119,8 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim,
                                              int32_t max_context_len, int32_t partition_size) {
-  (void)num_kv_heads;
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  const int32_t ptok = choose_partition(partition_size);
+  const int32_t ptok = choose_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
   if (ptok <= 0) return 0;
   const int64_t P = num_partitions(max_context_len, ptok);
   if (P <= 1) return 0;
@@ -136,7 +144,7 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID, "null pointer argument");
   if ((int64_t)num_seqs * num_kv_heads > INT32_MAX) return fail(PKV_ERR_INVALID, "too many sequences");
-  const int32_t ptok = choose_partition(partition_size);
+  const int32_t ptok = choose_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
   if (ptok % block_size || ptok > kMaxPartitionTokens)
     return fail(PKV_ERR_INVALID, "partition_size %d must be a multiple of %d and <= %d",
                 partition_size, block_size, kMaxPartitionTokens);

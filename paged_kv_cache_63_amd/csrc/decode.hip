@@ -56,11 +56,21 @@ __device__ __forceinline__ int usable_len(const DecodeArgs& a, int s) {
 }
 
 // ---------------------------------------------------------------- bf16 pass 1
-template <int D, int NW>
+// Workgroup = NW waves on one (sequence, KV head, partition); wave w takes
+// blocks w, w+NW, w+2NW, ... of the partition.  Each wave keeps DEPTH blocks
+// of K/V loads in flight in a ring of DEPTH+1 register buffers (indices fixed
+// by unrolling) while it computes on the oldest; the loads are non-temporal
+// (every K/V byte is read once per call).  No load is conditional: the trip
+// count is padded to a multiple of the ring size, padded slots re-read the
+// wave's last block and are computed fully masked.  Scheduling barriers keep
+// the compiler from hoisting a later block's products (and hence its load
+// wait) above the current block.
+template <int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * kWave) void decode_bf16_kernel(DecodeArgs a) {
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   constexpr int KQ = D / 32;  // QK products per block
   constexpr int KV = D / 16;  // PV products per block
+  constexpr int NBUF = DEPTH + 1;
   const int hkv = a.num_kv_heads;
   const int hq = a.num_q_heads;
   const int g = hq / hkv;
@@ -118,39 +128,35 @@ __global__ __launch_bounds__(NW * kWave) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
   for (int m = 0; m < KV; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 kf[KQ];
-  u32x2 vf[KV];
-  auto load_block = [&](int i, bf16x8* kd, u32x2* vd) {
+  bf16x8 kb[NBUF][KQ];
+  u32x2 vb[NBUF][KV];
+  auto load = [&](int i, bf16x8* kd, u32x2* vd) {
     const int phys = __builtin_amdgcn_readlane(my_entry, i);
     const int64_t base = ((int64_t)phys * hkv + h) * head_elems;
-    const uint16_t* kb = kpool + base + col * D + grp * 8;          // token row = col
-    const uint16_t* vb = vpool + base + col * kBs + grp * 4;        // channel row = col
+    const uint16_t* kr = kpool + base + col * D + grp * 8;    // token row = col
+    const uint16_t* vr = vpool + base + col * kBs + grp * 4;  // channel row = col
 #pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) kd[kk] = *reinterpret_cast<const bf16x8*>(kb + kk * 32);
+    for (int kk = 0; kk < KQ; ++kk)
+      kd[kk] = __builtin_bit_cast(
+          bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + kk * 32)));
 #pragma unroll
-    for (int m = 0; m < KV; ++m) vd[m] = *reinterpret_cast<const u32x2*>(vb + m * 16 * kBs);
+    for (int m = 0; m < KV; ++m)
+      vd[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vr + m * 16 * kBs));
   };
-
-  if (my_cnt > 0) load_block(0, kf, vf);
-  for (int i = 0; i < my_cnt; ++i) {
-    bf16x8 kn[KQ];
-    u32x2 vn[KV];
-    if (i + 1 < my_cnt) load_block(i + 1, kn, vn);
-
-    const int b = b0 + wave + i * NW;
-    const int nvalid = L - b * kBs;  // >= 1; >= 16 means the block is full
-
+  auto compute = [&](int i, const bf16x8* kd, const u32x2* vd) {
+    // tokens of this block inside the context; 0 for a padded slot
+    const int nvalid = i < my_cnt ? L - (b0 + wave + i * NW) * kBs : 0;
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], sc, 0, 0, 0);
-
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kd[kk], qf[kk], sc, 0, 0, 0);
     float z[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[r] = (grp * 4 + r < nvalid) ? sc[r] * sl2 : -INFINITY;
     float mb = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mb = fmaxf(mb, wave_xor(mb, 16));
     mb = fmaxf(mb, wave_xor(mb, 32));
+    // a padded slot leaves every value as it is (its mb is -inf)
     const float m_new = fmaxf(m_run, mb);
     const float alpha = exp2f(m_run - m_new);
     float p[4];
@@ -160,7 +166,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_bf16_kernel(DecodeArgs a) {
     m_run = m_new;
 #pragma unroll
     for (int m = 0; m < KV; ++m) o[m] *= alpha;
-
     // Tail tokens of a partly filled block hold arbitrary bits (possibly
     // NaN); p is 0 there but 0 * NaN is not, so clear those value words.
     const int t0 = grp * 4;
@@ -169,16 +174,27 @@ __global__ __launch_bounds__(NW * kWave) void decode_bf16_kernel(DecodeArgs a) {
     const bf16x4 pf = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
 #pragma unroll
     for (int m = 0; m < KV; ++m) {
-      const u32x2 vm = u32x2{vf[m].x & mx, vf[m].y & my};
+      const u32x2 vm = u32x2{vd[m].x & mx, vd[m].y & my};
       o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vm), pf, o[m],
                                                        0, 0, 0);
     }
+  };
 
-    if (i + 1 < my_cnt) {
+  if (my_cnt > 0) {
+    const int cnt_pad = (my_cnt + NBUF - 1) / NBUF * NBUF;
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) kf[kk] = kn[kk];
+    for (int j = 0; j < DEPTH; ++j) {
+      load(min(j, my_cnt - 1), kb[j], vb[j]);
+      __builtin_amdgcn_sched_barrier(0);  // buffers complete in ring order
+    }
+    for (int i = 0; i < cnt_pad; i += NBUF) {
 #pragma unroll
-      for (int m = 0; m < KV; ++m) vf[m] = vn[m];
+      for (int j = 0; j < NBUF; ++j) {
+        const int bi = i + j;
+        load(min(bi + DEPTH, my_cnt - 1), kb[(j + DEPTH) % NBUF], vb[(j + DEPTH) % NBUF]);
+        compute(bi, kb[j], vb[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -193,8 +209,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_bf16_kernel(DecodeArgs a) {
   if (col < g) {
 #pragma unroll
     for (int m = 0; m < KV; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[(wave * g + col) * D + m * 16 + grp * 4 + r] = o[m][r];
+      *reinterpret_cast<f32x4*>(&sm_o[(wave * g + col) * D + m * 16 + grp * 4]) = o[m];
     if (grp == 0) {
       sm_m[wave * 16 + col] = m_run;
       sm_l[wave * 16 + col] = l_run;
@@ -334,10 +349,13 @@ __global__ __launch_bounds__(kWave) void decode_f32_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ pass 2
+// One wave per (sequence, query head).  Lanes read the partitions' (m, l) in
+// strides of 64, the wave reduces M and the weights w_p = l_p e^(m_p - M);
+// each lane then accumulates its D/64 channels over the partitions, the
+// weights broadcast lane by lane.
 template <int D, bool BF16>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  extern __shared__ float w_s[];  // [P] weights, then reduction scratch
-  __shared__ float red[D / kWave];
+__global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int CPL = D / kWave;  // channels per lane (adjacent)
   const int j = blockIdx.x;       // query head
   const int s = blockIdx.y;
   const int hq = a.num_q_heads;
@@ -349,37 +367,42 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int64_t row = (int64_t)s * hq + j;
   const float* m = a.part_m + row * P;
   const float* l = a.part_l + row * P;
-  const int tid = threadIdx.x;
+  const float* o = a.part_o + row * P * D + threadIdx.x * CPL;
+  const int lane = threadIdx.x;
 
   float M = -INFINITY;
-  for (int p = tid; p < n_part; p += D) M = fmaxf(M, m[p]);
+  for (int p = lane; p < n_part; p += kWave) M = fmaxf(M, m[p]);
   for (int k = kWave / 2; k > 0; k >>= 1) M = fmaxf(M, wave_xor(M, k));
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int w = 1; w < D / kWave; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
 
   float W = 0.f;
-  for (int p = tid; p < n_part; p += D) {
-    const float wp = l[p] * expf(m[p] - M);
-    w_s[p] = wp;
-    W += wp;
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int p0 = 0; p0 < n_part; p0 += kWave) {
+    const int p = p0 + lane;
+    const float w = p < n_part ? l[p] * expf(m[p] - M) : 0.f;
+    W += w;
+    const int cnt = min(kWave, n_part - p0);
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+      const float* op = o + (int64_t)(p0 + k) * D;
+      if constexpr (CPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(op);
+        acc[0] = fmaf(wk, v.x, acc[0]);
+        acc[1] = fmaf(wk, v.y, acc[1]);
+      } else {
+        acc[0] = fmaf(wk, op[0], acc[0]);
+      }
+    }
   }
   for (int k = kWave / 2; k > 0; k >>= 1) W += wave_xor(W, k);
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = W;
-  __syncthreads();
-  W = 0.f;
+  const float inv = 1.f / W;
 #pragma unroll
-  for (int w = 0; w < D / kWave; ++w) W += red[w];
-
-  const float* o = a.part_o + row * P * D + tid;
-  float acc = 0.f;
-  for (int p = 0; p < n_part; ++p) acc = fmaf(w_s[p], o[(int64_t)p * D], acc);
-  const float res = acc / W;
-  if (BF16) ((uint16_t*)a.out)[row * D + tid] = f32_to_bf16(res);
-  else ((float*)a.out)[row * D + tid] = res;
+  for (int c = 0; c < CPL; ++c) {
+    const int d = lane * CPL + c;
+    if (BF16) ((uint16_t*)a.out)[row * D + d] = f32_to_bf16(acc[c] * inv);
+    else ((float*)a.out)[row * D + d] = acc[c] * inv;
+  }
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : -4; }
@@ -389,20 +412,20 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
   const dim3 grid(a.num_seqs * a.num_kv_heads, a.max_partitions);
   const int g = a.num_q_heads / a.num_kv_heads;
   if (dtype == 1) {
-    constexpr int NW = 4;
+    // 8 waves per workgroup, no register prefetch (4 waves per SIMD resident):
+    // the fastest of the depth / width combinations measured on MI355X.
+    constexpr int NW = 8;
     const size_t lds = (size_t)(NW * g * D + 2 * NW * 16) * sizeof(float);
-    decode_bf16_kernel<D, NW><<<grid, NW * kWave, lds, st>>>(a);
+    decode_bf16_kernel<D, NW, 0><<<grid, NW * kWave, lds, st>>>(a);
   } else {
     decode_f32_kernel<D><<<grid, kWave, 0, st>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return -4;
   if (a.max_partitions > 1) {
-    const size_t lds = (size_t)a.max_partitions * sizeof(float);
-    if (dtype == 1)
-      decode_merge_kernel<D, true><<<dim3(a.num_q_heads, a.num_seqs), D, lds, st>>>(a);
-    else
-      decode_merge_kernel<D, false><<<dim3(a.num_q_heads, a.num_seqs), D, lds, st>>>(a);
+    const dim3 mgrid(a.num_q_heads, a.num_seqs);
+    if (dtype == 1) decode_merge_kernel<D, true><<<mgrid, kWave, 0, st>>>(a);
+    else decode_merge_kernel<D, false><<<mgrid, kWave, 0, st>>>(a);
     e = hipGetLastError();
   }
   return status_of(e);

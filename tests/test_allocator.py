@@ -130,3 +130,21 @@ def test_free_order_validation():
 
 def test_kv_bytes_per_token():
     assert kv_bytes_per_token(32, 8, 128, 2) == 131072      # Llama-3-8B, bf16
+
+
+def test_truncate_returns_blocks_and_keeps_shared_ones():
+    lib = BlockAllocator(20, 4, max_seqs=4, free_order=list(range(20)))
+    a = lib.new_seq()
+    lib.append_tokens(a, 10)                      # blocks 0,1,2
+    b = lib.fork(a)[0]
+    lib.truncate(a, 5)                            # a keeps blocks 0,1 (ceil(5/4)=2)
+    assert lib.block_table(a).tolist() == [0, 1] and lib.context_len(a) == 5
+    assert lib.refcount(2) == 1 and lib.num_free() == 17   # block 2 still held by b
+    lib.validate()
+    lib.truncate(b, 0)
+    assert lib.refcount(2) == 0 and lib.refcount(0) == 1
+    lib.validate()
+    s, pairs = lib.append_tokens(a, 1)            # position 5 in shared? no: block 1 ref 1
+    assert len(pairs) == 0 and s.tolist() == [1 * 4 + 1]
+    with pytest.raises(ValueError):
+        lib.truncate(a, 99)

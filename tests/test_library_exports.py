@@ -54,7 +54,8 @@ def test_workspace_size_formula(lib):
     # 64 seqs, 32 q heads, D=128, contexts up to 4096, 512-token partitions -> 8 partitions
     assert ws(64, 32, 8, 128, 4096, 512) == 64 * 32 * 8 * 130 * 4
     assert ws(64, 32, 8, 128, 512, 512) == 0          # one partition: no workspace
-    assert ws(8, 64, 8, 128, 131072, 0) == 8 * 64 * 256 * 130 * 4   # default 512 tokens
+    assert ws(8, 64, 8, 128, 131072, 0) == 8 * 64 * 128 * 130 * 4   # library picks 1024 here
+    assert ws(1, 8, 1, 128, 8192, 0) == 1 * 8 * 32 * 130 * 4        # few pairs: 256 tokens
 
 
 @pytest.mark.parametrize("dtype,hd,bs,code", [(7, 128, 16, -2), (1, 96, 16, -2), (1, 128, 32, -2)])
