@@ -14,7 +14,10 @@ oracle reproduces, element for element):
   * K pool: ``[num_blocks][num_kv_heads][B][head_dim]`` -- one token's key is a
     contiguous row of ``head_dim`` words.
   * V pool: ``[num_blocks][num_kv_heads][head_dim][B]`` -- within a block the
-    value vectors are stored transposed, one row of B tokens per channel.
+    value vectors are stored transposed, one row of B tokens per channel,
+    and inside a row the token at offset ``off`` sits at position
+    ``v_pos(off)``: bits 2 and 3 of the offset exchanged (for B = 16 the
+    order is tokens 0-3, 8-11, 4-7, 12-15; the map is its own inverse).
 
 A *slot* names one token position in the pool: ``slot = phys_block * B + off``
 with ``off`` in ``[0, B)``.  Logical position ``pos`` of a sequence lives in
@@ -24,6 +27,12 @@ slot ``table[pos // B] * B + pos % B``.
 import numpy as np
 
 from .numerics import STORAGE_WORD, nan_word
+
+
+def v_pos(off):
+    """Position of a block's token ``off`` inside a V channel row (bits 2
+    and 3 exchanged).  Works on ints and integer arrays."""
+    return (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1)
 
 
 def slot_of(table_row, pos: int, block_size: int) -> int:
@@ -64,7 +73,7 @@ def append(k_pool, v_pool, k_new, v_new, slot_mapping, block_size: int) -> None:
             continue
         blk, off = s // block_size, s % block_size
         k_pool[blk, :, off, :] = k_new[t]
-        v_pool[blk, :, :, off] = v_new[t]
+        v_pool[blk, :, :, v_pos(off)] = v_new[t]
 
 
 def copy_blocks(k_pool, v_pool, block_mapping) -> None:
@@ -98,7 +107,7 @@ def gather(k_pool, v_pool, table_row, context_len: int, block_size: int):
         blk = int(table_row[pos // block_size])
         off = pos % block_size
         k_out[pos] = k_pool[blk, :, off, :]
-        v_out[pos] = v_pool[blk, :, :, off]
+        v_out[pos] = v_pool[blk, :, :, v_pos(off)]
     return k_out, v_out
 
 
@@ -111,7 +120,7 @@ def gather_fast(k_pool, v_pool, table_row, context_len: int, block_size: int):
     nblk = -(-context_len // block_size)
     ids = np.asarray(table_row[:nblk], dtype=np.int64)
     kb = k_pool[ids]                               # [nblk][Hkv][B][D]
-    vb = v_pool[ids]                               # [nblk][Hkv][D][B]
+    vb = v_pool[ids][..., v_pos(np.arange(block_size))]   # [nblk][Hkv][D][B], token order
     _, hkv, _, d = k_pool.shape
     k_out = kb.transpose(0, 2, 1, 3).reshape(nblk * block_size, hkv, d)[:context_len]
     v_out = vb.transpose(0, 3, 1, 2).reshape(nblk * block_size, hkv, d)[:context_len]

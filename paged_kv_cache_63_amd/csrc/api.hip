@@ -214,6 +214,7 @@ int paged_attention_extend(void* out, const void* q, const int32_t* cu_seqlens_q
   a.num_reqs = num_reqs;
   a.total_q = total_q;
   a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_q_heads = num_q_heads;

@@ -9,7 +9,9 @@ namespace pkv {
 // ---- vector types for the matrix-core builtins and wide memory accesses ----
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -19,6 +21,14 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t w) { return __uint_as_float((uint32_t)w << 16); }
+
+// Position of in-block token offset `off` inside a V channel row: bits 2 and
+// 3 exchanged, so a row holds tokens 0-3, 8-11, 4-7, 12-15.  A matrix-core
+// operand that needs tokens {4G..4G+3, 8+4G..8+4G+3} then reads 16
+// contiguous bytes.  The map is its own inverse.
+__host__ __device__ __forceinline__ int v_pos(int off) {
+  return (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1);
+}
 
 // fp32 -> bf16 word, round to nearest even (the gfx950 conversion instruction)
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
@@ -78,6 +88,7 @@ struct ExtendArgs {
   int32_t num_reqs;
   int32_t total_q;
   int32_t max_q_len;
+  int32_t max_seq_len;
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t num_q_heads;

@@ -134,7 +134,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_bf16_kernel(DecodeArgs a) {
     const int phys = __builtin_amdgcn_readlane(my_entry, i);
     const int64_t base = ((int64_t)phys * hkv + h) * head_elems;
     const uint16_t* kr = kpool + base + col * D + grp * 8;    // token row = col
-    const uint16_t* vr = vpool + base + col * kBs + grp * 4;  // channel row = col
+    // channel row = col; tokens 4grp..4grp+3 sit at v_pos(4grp)
+    const uint16_t* vr = vpool + base + col * kBs + v_pos(grp * 4);
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk)
       kd[kk] = __builtin_bit_cast(
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kWave) void decode_f32_kernel(DecodeArgs a) {
         const float pt = expf(sc_s[j][t] - m_new);
         psum += pt;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pt, vb[(lane + i * kWave) * kBs + t], acc[i]);
+        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pt, vb[(lane + i * kWave) * kBs + v_pos(t)], acc[i]);
       }
       l_run[j] = l_run[j] * alpha + psum;
       m_run[j] = m_new;

@@ -1,9 +1,10 @@
 // Pool writes and reads that move bits only: append (token -> slot),
 // copy-on-write block copy, and the gather of one sequence's blocks.
 //
-// Pool layout: K [num_blocks][Hkv][B][D], V [num_blocks][Hkv][D][B].
-// Every thread moves one 16-byte piece of a key or value row; all offsets
-// are 64-bit.
+// Pool layout: K [num_blocks][Hkv][B][D], V [num_blocks][Hkv][D][B] with
+// the tokens of a V channel row in the order v_pos (bits 2 and 3 of the
+// in-block offset exchanged: 0-3, 8-11, 4-7, 12-15).  Every thread moves one
+// 16-byte piece of a key or value row; all offsets are 64-bit.
 #include "common.h"
 
 namespace pkv {
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     const int64_t head_base = ((int64_t)blk * hkv + h) * bs * row_bytes;  // bytes
     *reinterpret_cast<u32x4*>(k_pool + head_base + (int64_t)off * row_bytes + piece * 16) = kv;
     const int32_t c0 = piece * kPer;  // first channel of the piece
-    uint8_t* vrow = v_pool + head_base + ((int64_t)c0 * bs + off) * E;
+    uint8_t* vrow = v_pool + head_base + ((int64_t)c0 * bs + v_pos(off)) * E;
     if constexpr (E == 2) {
       const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     const int64_t dst = row * row_bytes + (int64_t)piece * 16;
     *reinterpret_cast<u32x4*>(k_out + dst) =
         *reinterpret_cast<const u32x4*>(k_pool + head_base + (int64_t)off * row_bytes + piece * 16);
-    const uint8_t* vrow = v_pool + head_base + ((int64_t)piece * kPer * bs + off) * E;
+    const uint8_t* vrow = v_pool + head_base + ((int64_t)piece * kPer * bs + v_pos(off)) * E;
     uint32_t w[4];
     if constexpr (E == 2) {
 #pragma unroll

@@ -37,17 +37,20 @@ def test_fp32_widening_exact():
 
 # ---------------------------------------------------------- paging: layout
 def test_pool_layout_by_hand():
-    """Token at slot 2*4+3 (block 2, offset 3), head 1, channel 5 lands at
-    k_pool[2, 1, 3, 5] and v_pool[2, 1, 5, 3] (the documented layout)."""
-    B, hkv, D = 4, 2, 6
+    """Token at slot 2*16+5 (block 2, offset 5), head 1, channel 5 lands at
+    k_pool[2, 1, 5, 5] and at v_pool[2, 1, 5, 9] (offset 5 = 0b0101 sits at
+    position 0b1001 of the channel row: bits 2 and 3 exchanged)."""
+    B, hkv, D = 16, 2, 6
     kp, vp = paging.new_pools(5, hkv, D, B, "fp32")
     k_new = np.arange(hkv * D, dtype=np.uint32).reshape(1, hkv, D) + 100
     v_new = np.arange(hkv * D, dtype=np.uint32).reshape(1, hkv, D) + 500
-    paging.append(kp, vp, k_new, v_new, np.array([11]), B)
-    assert kp[2, 1, 3, 5] == 100 + 1 * D + 5
-    assert vp[2, 1, 5, 3] == 500 + 1 * D + 5
+    paging.append(kp, vp, k_new, v_new, np.array([2 * 16 + 5]), B)
+    assert kp[2, 1, 5, 5] == 100 + 1 * D + 5
+    assert vp[2, 1, 5, 9] == 500 + 1 * D + 5
     nan = numerics.nan_word("fp32")
     assert (kp != nan).sum() == hkv * D and (vp != nan).sum() == hkv * D
+    assert [int(paging.v_pos(o)) for o in range(16)] == [0, 1, 2, 3, 8, 9, 10, 11,
+                                                       4, 5, 6, 7, 12, 13, 14, 15]
 
 
 def test_append_skips_negative_slots():
