@@ -40,9 +40,18 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# The attention kernels never let a NaN reach a max or an exponential (masked
+# scores are replaced by -inf by index before use), so they are built without
+# NaN-preserving min/max semantics (no quieting instruction per operand).
+PER_FILE = {
+    "decode.hip": ["-fno-honor-nans"],
+    "extend.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -62,6 +71,13 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # A kernel whose host-side stub was not emitted links fine but fails at
+    # load time; refuse such a library here.
+    r = subprocess.run(["nm", "-D", "--undefined-only", "-C", tmp], capture_output=True, text=True)
+    missing = [l.strip() for l in r.stdout.splitlines() if "pkv::" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("library has undefined symbols of its own:\n" + "\n".join(missing))
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")

@@ -163,34 +163,46 @@ __global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, i
 
   // Copy tile tk into stage st with direct-to-LDS loads.  Load i of wave w
   // fills LDS chunks (i*NW + w)*64 + lane; the global chunk each lane reads
-  // is chosen so that K rows land XOR-swizzled (chunk c of row r at c ^ r).
+  // is chosen so that K rows land XOR-swizzled (chunk c of row r at c ^ r)
+  // and each V channel row's two 16-byte halves are swapped on rows 4..7
+  // mod 8 (so 8 consecutive lanes reading half G of 8 rows hit distinct
+  // banks).  Which pool, which block of the tile and the byte offset inside
+  // the (block, head) slab do not change from tile to tile: computed once.
   // Blocks past the end of the sequence read block 0 of the pool (masked
   // out when used).
+  int64_t src_off[PER_T];   // byte offset inside the (K or V) pool, block 0
+  int src_blk[PER_T];
+  bool src_v[PER_T];
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    const int c = (i * NW + wave) * kWave + lane;
+    const int which = c / (TILEB / 16);
+    const int cc = c - which * (TILEB / 16);
+    const int blk = cc / (BLKB / 16);
+    const int within = cc - blk * (BLKB / 16);
+    int src_chunk;
+    if (which == 0) {
+      const int row = within / CPR;
+      const int pos = within - row * CPR;
+      src_chunk = row * CPR + (pos ^ (row % CPR));
+    } else {
+      src_chunk = within ^ ((within >> 3) & 1);
+    }
+    src_off[i] = (int64_t)h * BLKB + src_chunk * 16;
+    src_blk[i] = blk;
+    src_v[i] = which != 0;
+  }
+  const int64_t blk_stride = (int64_t)hkv * BLKB;   // bytes between physical blocks
   auto issue = [&](int tk, int st) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int c0 = (i * NW + wave) * kWave;  // first LDS chunk of this load
-      const int c = c0 + lane;
-      const int which = c / (TILEB / 16);
-      const int cc = c - which * (TILEB / 16);
-      const int blk = cc / (BLKB / 16);
-      const int within = cc - blk * (BLKB / 16);
-      int src_chunk = within;
-      if (which == 0) {
-        const int row = within / CPR;
-        const int pos = within - row * CPR;
-        src_chunk = row * CPR + (pos ^ (row % CPR));
-      } else {
-        // V channel row = two 16-byte halves; rows 4..7 mod 8 store them
-        // swapped so 8 consecutive lanes reading half G of 8 rows hit
-        // distinct banks
-        src_chunk = within ^ ((within >> 3) & 1);
-      }
-      const int kb = tk * NBT + blk;
+      const int kb = tk * NBT + src_blk[i];
       const int phys = kb < nblk ? entry(kb) : 0;
-      const uint8_t* src = (which ? vpool : kpool) + ((int64_t)phys * hkv + h) * BLKB + src_chunk * 16;
+      const uint8_t* src = (src_v[i] ? vpool : kpool) + src_off[i] + (int64_t)phys * blk_stride;
       __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(&kv_s[st][c0 * 16]), 16, 0, 0);
+          src,
+          (__attribute__((address_space(3))) void*)(&kv_s[st][c0 * 16]), 16, 0, 0);
     }
   };
 
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, i
       const bool grow = m_new > m_ref + kLazy;
       if (__any(grow)) {   // rare after the first tile
         const float target = grow ? m_new : m_ref;
-        const float alpha = exp2f(m_ref - target);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - target);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
@@ -267,7 +279,7 @@ __global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, i
       for (int b = 0; b < NBT; ++b) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = exp2f(fmaf(sc[b >> 1][(b & 1) * 8 + e], c2, nm));
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[b >> 1][(b & 1) * 8 + e], c2, nm));
         const bf16x8 pb = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                                  (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
         pf[b] = pb;
