@@ -3,25 +3,38 @@
 // Request r has n new tokens at positions P..P+n-1 (P = seq_len - n); token
 // i attends to keys 0..P+i.  Their keys/values are already in the pool.
 //
-// bf16 kernel: one workgroup = 4 waves = one KV head of one request x a tile
-// of ROWS query rows, where a row is (new token, query head of the group) and
+// bf16 kernel: one workgroup = 8 waves = one KV head of one request x a tile
+// of 256 query rows, where a row is (new token, query head of the group) and
 // rows of consecutive tokens are adjacent (row = token * g + head), so every
-// staged K/V tile serves the whole GQA group.  Each wave owns 16*CT rows.
-// Keys are consumed 64 at a time (four 16-token blocks): the workgroup copies
-// the four K blocks and four V blocks of the next tile from the pool into a
-// second LDS buffer while it computes on the current one (global loads are
-// issued before the compute, LDS writes after it, one barrier per tile).
-// Per 64-key tile and 16 rows a wave issues, on the matrix cores,
-//   S^T[key x row]  = K[key x D] . Q^T[D x row]        (16x16x32 bf16)
-//   O^T[D x row]   += V^T[D x key] . P^T[key x row]    (16x16x32 bf16)
-// The score tile's register layout is the layout P^T needs as an operand
-// (row = lane column, four consecutive keys per lane and block), and V is
-// stored channel-major in the pool, so neither product needs a transpose.
-// Softmax is online (running max / sum per row, base-2 exponentials with
-// the scale folded in), fp32.  The causal mask is applied only on the tiles
-// that cross a wave's diagonal; tiles wholly in a wave's future are skipped.
-// K rows are XOR-swizzled in LDS (16-byte chunk c of row i stored at chunk
-// c ^ i) so the 16 rows a fragment load touches hit distinct banks.
+// staged K/V tile serves the whole GQA group.  Each wave owns 32 rows.
+// Keys are consumed 64 at a time (four 16-token blocks), copied from the
+// pool by direct-to-LDS loads into a 5-stage LDS ring (160 KB for D = 128),
+// three tiles ahead of their first use.  Per 64-key tile a wave issues, on
+// the matrix cores (v_mfma_f32_32x32x16_bf16),
+//   S^T[key x row]  = K[key x D] . Q^T[D x row]
+//   O^T[D x row]   += V^T[D x key] . P^T[key x row]
+// The score tile's register layout is the layout P^T needs as an operand,
+// and V is stored channel-major in the pool, so neither product needs a
+// transpose.  Softmax is online (running max / sum per row, base-2
+// exponentials with the scale folded in), fp32.
+//
+// Ping-pong: waves w and w+4 share a SIMD.  Every wave alternates a matrix
+// phase (PV of the previous tile, then QK of the current one: 32 MFMAs fed
+// from LDS) and a vector phase (softmax of the current tile, plus the tile
+// copies, table lookups and the first LDS reads of the next matrix phase),
+// with a workgroup barrier after every phase, and waves 4..7 run one phase
+// behind waves 0..3.  So while one wave of a SIMD keeps its matrix core
+// busy, the other runs its exponentials on the vector ALU.  The softmax
+// uses no instruction that executes on the matrix pipeline (the bf16 dot
+// products would wait for the other wave's MFMAs), and its results are
+// pinned to the vector phase (the compiler would otherwise sink them into
+// the matrix phase that consumes them).
+//
+// LDS layouts (16-byte chunks; reads hit 64 distinct banks per 16 lanes):
+// K rows are XOR-swizzled (chunk c of row i at c ^ f(i)); each V channel
+// row's two 16-byte halves are swapped where bit 2 xor bit 3 of the channel
+// is set.  The direct-to-LDS copy writes LDS contiguously, so each lane reads
+// the global chunk that belongs at its LDS position.
 //
 // Work order: all query tiles of one (request, KV head) read the same keys,
 // so they are given workgroup ids that land on the same XCD (ids are dealt
@@ -32,6 +45,8 @@
 // exact expf; it serves fp32 inputs.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pkv {
@@ -40,9 +55,16 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBs = 16;
 constexpr int kXcds = 8;
-constexpr int kTabLdsMax = 12288;  // block-table entries that fit in LDS beside the K/V ring
 
-__device__ __forceinline__ float wave_xor(float x, int mask) { return __shfl_xor(x, mask, kWave); }
+// x combined with the value of lane l ^ 32, through the VALU (no LDS).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // s_waitcnt with only the vector-memory counter constrained (expcnt and
 // lgkmcnt left at their maxima), gfx9 encoding.
@@ -52,12 +74,45 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// TAB_LDS: the request's whole block table sits in LDS (tab_cap entries,
-// dynamic shared memory), so the loop issues no global loads other than
-// the direct-to-LDS tile copies and every wait on the vector-memory counter
-// is exact.  Otherwise table entries are read from global memory per tile
-// (for contexts too long for the LDS table; the waits then cover them).
-//
+// Workgroup barrier that also keeps the compiler from moving memory
+// operations across it (the hardware barrier alone does not wait for
+// anything; the LDS data it publishes was waited for explicitly).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// Marks a register value as produced here: the computation of x cannot be
+// moved past this point (the compiler otherwise sinks pure ALU work across
+// workgroup barriers towards its first use).
+template <typename T>
+__device__ __forceinline__ void materialize(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// One direct-to-LDS copy: every lane loads 16 bytes from sbase + voff
+// (sbase wave-uniform) and the wave writes them to LDS at lds + lane*16.
+// Issued as inline assembly so that the compiler neither hoists 64-bit
+// per-lane addresses out of the loop nor adds waits for these copies
+// before unrelated LDS reads; the kernel waits for them itself (vmcnt).
+// M0 (the LDS base of the copy) is saved and restored around it; the
+// s_nop covers the M0-write hazard.
+__device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16, A 32x16, B 16x32, C 32x32;
 // lane l: A/B row-or-column l%32, k slots 8*(l/32)..+7; C column l%32, rows
 // 8*(v/4) + 4*(l/32) + v%4 for its 16 values v):
@@ -68,9 +123,11 @@ __device__ __forceinline__ void wait_vm() {
 // block and 8..15 the second, in exactly the slot order P^T needs when V^T
 // slot (hb, e) holds key 8*hb + 4G + e, i.e. two 8-byte reads of a
 // channel's 32-byte row.  No shuffles between the two products.
-template <int D, int NW, bool TAB_LDS>
-__global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, int tiles_per_unit,
-                                                                 int units, int tab_cap) {
+template <int D>
+__global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, int tiles_per_unit,
+                                                                int units) {
+  constexpr int NW = 8;
+  constexpr int HALF = NW / 2;            // waves per group: one per SIMD
   constexpr int RPW = 32;                 // query rows per wave
   constexpr int ROWS = NW * RPW;
   constexpr int NBT = 4;                  // blocks per key tile
@@ -79,19 +136,19 @@ __global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, i
   constexpr int DT = D / 32;              // 32-channel tiles of O
   constexpr int ROWB = D * 2;             // bytes of one key row
   constexpr int CPR = D / 8;              // 16-byte chunks per key row
+  constexpr int SWZ = 16 / CPR;           // consecutive key rows sharing one swizzle value
   constexpr int BLKB = kBs * ROWB;        // bytes of one (block, head) slab
   constexpr int TILEB = NBT * BLKB;       // bytes of a K (or V) tile
-  constexpr int CHUNKS = 2 * TILEB / 16;  // K + V chunks per tile
-  constexpr int PER_T = CHUNKS / (NW * kWave);  // direct-to-LDS loads per thread per tile
-  constexpr int NST = 3;                  // LDS ring stages (loads run two tiles ahead)
-  static_assert(PER_T * NW * kWave == CHUNKS, "tile must split evenly over the threads");
+  constexpr int SEGS = TILEB / 16 / kWave;  // 64-chunk segments per K (or V) tile
+  constexpr int PER_T = 2 * SEGS / NW;    // direct-to-LDS loads per thread per tile
+  constexpr int NST = 5;                  // LDS ring stages (160 KB for D = 128)
+  static_assert(PER_T * NW == 2 * SEGS, "tile must split evenly over the waves");
   // Rescale the accumulators only when a row's maximum has grown by more
   // than this many powers of two since the reference used for its
   // exponentials (the exponentials stay below 2^kLazy in between).
   constexpr float kLazy = 8.0f;
 
   __shared__ __attribute__((aligned(16))) uint8_t kv_s[NST][2 * TILEB];  // [stage][K tile | V tile]
-  extern __shared__ int32_t tab_s[];      // [tab_cap] when TAB_LDS
 
   const int hkv = a.num_kv_heads;
   const int hq = a.num_q_heads;
@@ -109,25 +166,25 @@ __global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, i
   const int row0 = tile * ROWS;
   if (n <= 0 || row0 >= n * g || q0 < 0 || q0 + n > a.total_q) return;
   if (L > a.max_blocks_per_seq * kBs) L = a.max_blocks_per_seq * kBs;
-  if (TAB_LDS && L > tab_cap * kBs) L = tab_cap * kBs;
   const int P = L - n;
   if (P < 0) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const bool lead = wave < HALF;
   const int c32 = lane & 31;    // A/B row-or-column, C column
   const int G = lane >> 5;      // k-slot group / C row group
   const int nblk = (L + kBs - 1) / kBs;
-  const int32_t* trow = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
+  const_i32* trow = (const_i32*)(a.block_tables + (int64_t)r * a.max_blocks_per_seq);
 
   // Rows of this workgroup and their last visible key.
   const int last_row = min(row0 + ROWS, n * g) - 1;
   const int kend = P + last_row / g + 1;                   // keys 0..kend-1 are needed
   const int ntiles = (kend + KT - 1) / KT;
   const int wrow0 = row0 + wave * RPW;
+  const bool has_rows = wrow0 <= last_row;
   const int wq_min = P + min(wrow0, last_row) / g;         // smallest query position of the wave
-  const int wq_max = P + min(wrow0 + RPW - 1, last_row) / g;
+  const int wq_max = has_rows ? P + min(wrow0 + RPW - 1, last_row) / g : -1;
 
   // Q^T operand: lane (row c32, group G) holds channels ks*16 + G*8 .. +7.
   const uint16_t* qp = (const uint16_t*)a.q;
@@ -146,65 +203,74 @@ __global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, i
       qf[ks] = live ? v : bf16x8{};
     }
   }
-  if (TAB_LDS)
-    for (int i = tid; i < nblk; i += NW * kWave) {
-      const int b = trow[i];
-      tab_s[i] = (b >= 0 && b < a.num_blocks) ? b : 0;
-    }
-  __syncthreads();  // table in LDS, Q loaded (no vector loads outstanding)
 
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
   const uint8_t* vpool = (const uint8_t*)a.v_pool;
-  auto entry = [&](int b) -> int {
-    if (TAB_LDS) return tab_s[b];
-    const int e = trow[b];
-    return (e >= 0 && e < a.num_blocks) ? e : 0;
+  // Physical block of logical block kb (block 0 past the end of the
+  // sequence or for an invalid entry; such keys are masked where used).
+  // The table word is loaded well before its copy is issued and checked
+  // only then, so the scalar load's latency stays off the critical path.
+  auto entry_raw = [&](int kb) -> int { return trow[kb < nblk ? kb : 0]; };
+  auto entry_ok = [&](int kb, int e) -> int {
+    return (kb < nblk && e >= 0 && e < a.num_blocks) ? e : 0;
   };
 
-  // Copy tile tk into stage st with direct-to-LDS loads.  Load i of wave w
-  // fills LDS chunks (i*NW + w)*64 + lane; the global chunk each lane reads
-  // is chosen so that K rows land XOR-swizzled (chunk c of row r at c ^ r)
-  // and each V channel row's two 16-byte halves are swapped on rows 4..7
-  // mod 8 (so 8 consecutive lanes reading half G of 8 rows hit distinct
-  // banks).  Which pool, which block of the tile and the byte offset inside
-  // the (block, head) slab do not change from tile to tile: computed once.
-  // Blocks past the end of the sequence read block 0 of the pool (masked
-  // out when used).
-  int64_t src_off[PER_T];   // byte offset inside the (K or V) pool, block 0
+  // Direct-to-LDS copy of tile t into stage st.  Load i of wave w fills the
+  // 64-chunk segment s = i*NW + w of the stage ([K tile | V tile]); which
+  // pool, which block of the tile and each lane's byte offset inside the
+  // head's slab are fixed per (i, w): computed once.
+  uint32_t src_off[PER_T];
   int src_blk[PER_T];
   bool src_v[PER_T];
 #pragma unroll
   for (int i = 0; i < PER_T; ++i) {
-    const int c = (i * NW + wave) * kWave + lane;
-    const int which = c / (TILEB / 16);
-    const int cc = c - which * (TILEB / 16);
-    const int blk = cc / (BLKB / 16);
-    const int within = cc - blk * (BLKB / 16);
+    const int s = i * NW + wave;
+    const int which = s / SEGS;
+    const int c0 = (s - which * SEGS) * kWave;   // first chunk of the segment in its tile
+    const int blk = c0 / (BLKB / 16);
+    const int within = c0 - blk * (BLKB / 16) + lane;
     int src_chunk;
     if (which == 0) {
       const int row = within / CPR;
       const int pos = within - row * CPR;
-      src_chunk = row * CPR + (pos ^ (row % CPR));
+      src_chunk = row * CPR + (pos ^ ((row / SWZ) % CPR));
     } else {
-      src_chunk = within ^ ((within >> 3) & 1);
+      const int row = within >> 1;
+      src_chunk = within ^ (((row >> 2) ^ (row >> 3)) & 1);
     }
-    src_off[i] = (int64_t)h * BLKB + src_chunk * 16;
+    src_off[i] = (uint32_t)(h * BLKB + src_chunk * 16);
     src_blk[i] = blk;
     src_v[i] = which != 0;
   }
   const int64_t blk_stride = (int64_t)hkv * BLKB;   // bytes between physical blocks
-  auto issue = [&](int tk, int st) {
+  auto fetch_entries = [&](int t, int (&e)[PER_T]) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) e[i] = entry_raw(t * NBT + src_blk[i]);
+  };
+  auto issue = [&](int t, const int (&e)[PER_T]) {
+    const int st = t % NST;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int c0 = (i * NW + wave) * kWave;  // first LDS chunk of this load
-      const int kb = tk * NBT + src_blk[i];
-      const int phys = kb < nblk ? entry(kb) : 0;
-      const uint8_t* src = (src_v[i] ? vpool : kpool) + src_off[i] + (int64_t)phys * blk_stride;
-      __builtin_amdgcn_global_load_lds(
-          src,
-          (__attribute__((address_space(3))) void*)(&kv_s[st][c0 * 16]), 16, 0, 0);
+      const int phys = entry_ok(t * NBT + src_blk[i], e[i]);
+      const uint8_t* base = (src_v[i] ? vpool : kpool) + (int64_t)phys * blk_stride;
+      const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)(
+          &kv_s[st][(i * NW + wave) * kWave * 16]);
+      lds_dma16(base, src_off[i], lds);
     }
   };
+
+  // LDS read offsets (stage 0).  K: key row c32 % 16 of block
+  // 2*chunk + c32 / 16, logical chunk 2*ks + G.  V: channel dt*32 + c32,
+  // half G of the row.
+  uint32_t koff[KS];
+  {
+    const int row = c32 & 15;
+    const int f = (row / SWZ) % CPR;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      koff[ks] = (uint32_t)((c32 >> 4) * BLKB + row * ROWB + (((ks * 2 + G) ^ f) * 16));
+  }
+  const uint32_t voff = (uint32_t)(TILEB + c32 * 32 + ((G ^ (((c32 >> 2) ^ (c32 >> 3)) & 1)) * 16));
 
   const float c2 = a.scale * kLog2e;   // scores -> base-2 exponent units
   float m_ref = -INFINITY, l_run = 0.f;
@@ -213,133 +279,255 @@ __global__ __launch_bounds__(NW * kWave) void extend_bf16_kernel(ExtendArgs a, i
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
-  const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
+  f32x16 sc[2];
+  bf16x8 pf[NBT];
 
-  // One barrier per tile: after it, tile tk is in LDS and every wave has
-  // finished tile tk-1, so stage (tk+2)%3 = (tk-1)%3 may be refilled.
-  issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
+  // Matrix-phase streams.  Fragment reads and MFMAs are interleaved with
+  // a fixed lookahead, so LDS latency hides behind the matrix core and only
+  // a few fragments are live at once.
+  // PV reads: V fragment (block b, channel tile dt) for i = b*DT + dt.
+  // QK reads: K fragment (k-step ks, 32-key chunk ch) for i = ks*2 + ch.
+  constexpr int NPV = NBT * DT;
+  constexpr int NQK = 2 * KS;
+  constexpr int LA = 6;          // lookahead of the QK-only stream
+  constexpr int NPRE = NPV / 2;  // V fragments read at the end of the vector phase
+  auto vread = [&](int st, int i) {
+    return *reinterpret_cast<const bf16x8*>(kv_s[st] + voff + (i / DT) * BLKB + (i % DT) * 32 * 32);
+  };
+  auto kread = [&](int st, int i) {
+    return *reinterpret_cast<const bf16x8*>(kv_s[st] + koff[i / 2] + (i % 2) * 2 * BLKB);
+  };
+  auto pv_mfma = [&](int i, bf16x8 f) {
+    o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / DT], o[i % DT], 0, 0, 0);
+  };
+  auto qk_mfma = [&](int i, bf16x8 f) {
+    sc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i / 2], sc[i % 2], 0, 0, 0);
+  };
+  auto clear_sc = [&]() {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[ch][v] = 0.f;
+  };
+  // The first NPRE V fragments of the next PV, read while this wave is in
+  // its vector phase (their tile is already in LDS), so the matrix phase
+  // starts on MFMAs rather than on LDS latency.
+  bf16x8 vpre[NPRE];
+  auto pre_read = [&](int sp) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) vpre[i] = vread(sp, i);
+  };
+  // PV of the tile in stage sp (fragments 0..NPRE-1 already read), then QK
+  // of the tile in stage sq.  Stream read j is issued after MFMA j and
+  // consumed by MFMA j + NPRE.
+  auto pv_qk = [&](int sp, int sq) {
+    constexpr int NR = NPV - NPRE + NQK;
+    bf16x8 fr[NR];
+#pragma unroll
+    for (int j = 0; j < NPV - NPRE; ++j) fr[j] = vread(sp, NPRE + j);
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) fr[NPV - NPRE + j] = kread(sq, j);
+    clear_sc();
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) pv_mfma(i, vpre[i]);
+#pragma unroll
+    for (int i = NPRE; i < NPV; ++i) pv_mfma(i, fr[i - NPRE]);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) qk_mfma(i, fr[NPV - NPRE + i]);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
+  };
+  // QK alone (first tile): LA reads, then (MFMA, read) pairs.
+  auto qk = [&](int sq) {
+    bf16x8 fr[NQK];
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) fr[i] = kread(sq, i);
+    clear_sc();
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) qk_mfma(i, fr[i]);
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+    for (int i = 0; i < NQK - LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+  };
 
-  for (int tk = 0; tk < ntiles; ++tk) {
-    const int st = tk % NST;
-    if (tk + 1 < ntiles) wait_vm<PER_T>();   // tile tk landed; tk+1 may be in flight
-    else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    if (tk + 2 < ntiles) issue(tk + 2, (tk + 2) % NST);
-
-    const int kbase = tk * KT;
-    if (kbase <= wq_max) {  // else the whole tile is in this wave's future
-      const uint8_t* ks_ = kv_s[st];
-      const uint8_t* vs = kv_s[st] + TILEB;
-      // S^T for the two 32-key chunks of the tile
-      f32x16 sc[2];
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        const int blk = 2 * ch + (c32 >> 4);
-        const int row = c32 & 15;
-        const uint8_t* krow = ks_ + blk * BLKB + row * ROWB;
-        f32x16 acc;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int cix = ks * 2 + G;
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ((cix ^ (row % CPR)) * 16));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc, 0, 0, 0);
-        }
-        sc[ch] = acc;
-      }
-
-      if (kbase + KT - 1 > wq_min) {   // tile crosses the diagonal of some row
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (kbase + ch * 32 + (v >> 2) * 8 + G * 4 + (v & 3) > qpos) sc[ch][v] = -INFINITY;
-      }
-      float mb = -INFINITY;
+  // Probabilities of tile t (keys kbase..) from its scores.
+  auto softmax = [&](int kbase, auto masked) {
+    if constexpr (decltype(masked)::value) {   // tile crosses the diagonal of some row
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) mb = fmaxf(mb, fmaxf(sc[ch][v], sc[ch][v + 1]));
-      mb = fmaxf(mb, wave_xor(mb, 32));
-      const float m_new = mb * c2;
-      const bool grow = m_new > m_ref + kLazy;
-      if (__any(grow)) {   // rare after the first tile
-        const float target = grow ? m_new : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - target);
-        l_run *= alpha;
+        for (int v = 0; v < 16; ++v)
+          if (kbase + ch * 32 + (v >> 2) * 8 + G * 4 + (v & 3) > qpos) sc[ch][v] = -INFINITY;
+    }
+    float mb = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        m_ref = target;
-      }
-      const float nm = -m_ref;
-      bf16x8 pf[NBT];
+    for (int v = 2; v < 32; v += 2) mb = fmaxf(fmaxf(mb, sc[v >> 4][v & 15]), sc[v >> 4][(v & 15) + 1]);
+    mb = max_halves(mb);
+    const float m_new = mb * c2;
+    const bool grow = m_new > m_ref + kLazy;
+    if (__any(grow)) {   // rare after the first tile
+      const float target = grow ? m_new : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - target);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m_ref = target;
+    }
+    const float nm = -m_ref;
+#pragma unroll
+    for (int b = 0; b < NBT; ++b) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[b >> 1][(b & 1) * 8 + e], c2, nm));
+      pf[b] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                     (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+      // Row sum in fp32 adds (of the unrounded probabilities): the bf16 dot
+      // instructions would run on the matrix pipeline and stall behind the
+      // other wave's MFMAs.
+      l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    // The probabilities are computed in this (vector) phase, not in the
+    // matrix phase that consumes them.
+#pragma unroll
+    for (int b = 0; b < NBT; ++b) materialize(pf[b]);
+    materialize(l_run);
+  };
+
+  // PV alone (the last tile of the workgroup).  V^T operand of block b,
+  // channel tile dt: the lane's 16 bytes are keys 4G..4G+3 and 8+4G..8+4G+3
+  // of channel dt*32 + c32 (positions 8G..8G+7 of the row).  Keys at or past
+  // the end of the sequence (tail of the last block, blocks read as block
+  // 0) hold arbitrary bits: p is 0 there but 0 * NaN is not, so their value
+  // words are cleared.
+  auto pv = [&](int sp, int kbase) {
+    bf16x8 fr[NPV];
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) fr[i] = vread(sp, i);
+    if (kbase + KT > L) {
 #pragma unroll
       for (int b = 0; b < NBT; ++b) {
-        float p[8];
+        uint32_t mk[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[b >> 1][(b & 1) * 8 + e], c2, nm));
-        const bf16x8 pb = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                                 (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-        pf[b] = pb;
-        // row sum of the rounded probabilities the PV product uses
-        const bf16x2* pp = reinterpret_cast<const bf16x2*>(&pb);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
-      }
-
-      // Keys at or past the end of the sequence (tail of the last block,
-      // blocks read as block 0) hold arbitrary bits: p is 0 there but 0 * NaN
-      // is not, so their value words are cleared (last tile only).
-      // V^T operand of block b, channel tile dt: the lane's 16 bytes are
-      // keys 4G..4G+3 and 8+4G..8+4G+3 of channel dt*32 + c32 (positions
-      // 8G..8G+7 of the row), i.e. half G of the row, stored at half
-      // G ^ ((row >> 2) & 1).
-      auto vptr = [&](int b, int dt) {
-        const int row = dt * 32 + c32;
-        return vs + b * BLKB + row * 32 + ((G ^ ((row >> 2) & 1)) * 16);
-      };
-      if (kbase + KT > L) {
-#pragma unroll
-        for (int b = 0; b < NBT; ++b) {
-          uint32_t mk[4];
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const int k0 = kbase + b * kBs + hb * 8 + G * 4;
-            mk[2 * hb] = (k0 < L ? 0x0000ffffu : 0u) | (k0 + 1 < L ? 0xffff0000u : 0u);
-            mk[2 * hb + 1] = (k0 + 2 < L ? 0x0000ffffu : 0u) | (k0 + 3 < L ? 0xffff0000u : 0u);
-          }
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(vptr(b, dt));
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, u32x4{w.x & mk[0], w.y & mk[1], w.z & mk[2], w.w & mk[3]});
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[b], o[dt], 0, 0, 0);
-          }
+        for (int hb = 0; hb < 2; ++hb) {
+          const int k0 = kbase + b * kBs + hb * 8 + G * 4;
+          mk[2 * hb] = (k0 < L ? 0x0000ffffu : 0u) | (k0 + 1 < L ? 0xffff0000u : 0u);
+          mk[2 * hb + 1] = (k0 + 2 < L ? 0x0000ffffu : 0u) | (k0 + 3 < L ? 0xffff0000u : 0u);
         }
-      } else {
 #pragma unroll
-        for (int b = 0; b < NBT; ++b)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vptr(b, dt));
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[b], o[dt], 0, 0, 0);
-          }
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x4 w = __builtin_bit_cast(u32x4, fr[b * DT + dt]);
+          fr[b * DT + dt] = __builtin_bit_cast(
+              bf16x8, u32x4{w.x & mk[0], w.y & mk[1], w.z & mk[2], w.w & mk[3]});
+        }
       }
     }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) pv_mfma(i, fr[i]);
+  };
+
+  // Slots: waves 0..3 run matrix phase j in slot 2j and vector phase j in
+  // slot 2j+1; waves 4..7 one slot later.  Matrix phase j holds PV of tile
+  // j-1 and QK of tile j; vector phase t the softmax of tile t, the copy of
+  // tile t+3 (tiles 0..2 are copied before the loop) and the table lookups
+  // for tile t+4, whether or not this wave computes on those tiles (all
+  // eight waves share each copy).  Tile t occupies stage t % 5 from its copy
+  // until the PV in matrix phase t+1, which every wave has left before any
+  // wave starts vector phase t+2, the first that may refill the stage.
+  //
+  // Phase boundary after the phase in slot s.  Odd slots end where tile
+  // (s+1)/2 must be in LDS for everyone: this wave waits for its share,
+  // leaving in flight only the copies it issued after that tile (waves
+  // 0..3 have issued up to tile u+3 by then, waves 4..7 up to u+2).
+  auto end_phase = [&](int s) {
+    if (s & 1) {
+      const int u = s >> 1;
+      const int n_out = min(u + (lead ? 3 : 2), ntiles - 1) - (u + 1);
+      if (n_out >= 2) wait_vm<2 * PER_T>();
+      else if (n_out == 1) wait_vm<PER_T>();
+      else wait_vm<0>();
+    }
+    wg_barrier();
+  };
+  int e_nxt[PER_T];   // physical blocks of the next tile to copy
+  auto copy_and_lookup = [&](int t) {
+    if (t + 3 < ntiles) issue(t + 3, e_nxt);
+    if (t + 4 < ntiles) fetch_entries(t + 4, e_nxt);
+  };
+
+  // This wave computes on tiles 0..nt-1 (later tiles are in the future of
+  // all its rows), with the causal mask from tile td on; a tile past the end
+  // of the sequence can only be the last one, whose PV has no QK after it.
+  const int nt = has_rows ? min(ntiles, wq_max / KT + 1) : 0;
+  const int td = (wq_min + 1) / KT;
+  {
+    int e0[PER_T], e1[PER_T], e2[PER_T];
+    fetch_entries(0, e0);
+    fetch_entries(1, e1);
+    fetch_entries(2, e2);
+    if (ntiles > 3) fetch_entries(3, e_nxt);
+    wait_vm<0>();   // Q fragments in registers before the copies are counted
+    issue(0, e0);
+    if (ntiles > 1) issue(1, e1);
+    if (ntiles > 2) issue(2, e2);
   }
+  if (ntiles > 2) wait_vm<2 * PER_T>();
+  else if (ntiles > 1) wait_vm<PER_T>();
+  else wait_vm<0>();
+  wg_barrier();
+  const int lag = lead ? 0 : 1;
+  if (!lead) wg_barrier();
+  if (nt > 0) qk(0);
+  int t = 0;
+  const int t_plain = min(td, nt - 1);
+  for (; t < t_plain; ++t) {          // no mask, PV and QK
+    end_phase(2 * t + lag);
+    copy_and_lookup(t);
+    softmax(t * KT, std::false_type{});
+    pre_read(t % NST);
+    end_phase(2 * t + 1 + lag);
+    pv_qk(t % NST, (t + 1) % NST);
+  }
+  for (; t < nt - 1; ++t) {           // masked, PV and QK
+    end_phase(2 * t + lag);
+    copy_and_lookup(t);
+    softmax(t * KT, std::true_type{});
+    pre_read(t % NST);
+    end_phase(2 * t + 1 + lag);
+    pv_qk(t % NST, (t + 1) % NST);
+  }
+  if (t < nt) {                        // last tile of this wave: PV only
+    end_phase(2 * t + lag);
+    copy_and_lookup(t);
+    if (t < td) softmax(t * KT, std::false_type{});
+    else softmax(t * KT, std::true_type{});
+    end_phase(2 * t + 1 + lag);
+    pv(t % NST, t * KT);
+    ++t;
+  }
+  for (; t < ntiles; ++t) {           // copies and barriers only
+    end_phase(2 * t + lag);
+    copy_and_lookup(t);
+    end_phase(2 * t + 1 + lag);
+  }
+  if (lead) wg_barrier();
 
   // Normalise and store: lane (row c32, group G) holds channels
   // dt*32 + 8*(v/4) + 4*G + v%4 of its row.
-  float l = l_run;
-  l += wave_xor(l, 32);
+  const float l = sum_halves(l_run);
   const int rr = wrow0 + c32;
   if (rr > last_row) return;
-  const int t = rr / g;
-  const int j = rr - t * g;
+  const int tok = rr / g;
+  const int jh = rr - tok * g;
   const float inv = 1.f / l;
-  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + t) * hq + h * g + j) * D + G * 4;
+  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + tok) * hq + h * g + jh) * D + G * 4;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -451,25 +639,7 @@ int launch_e(const ExtendArgs& a, int32_t dtype, hipStream_t st) {
     const int64_t grid = (int64_t)kXcds * unit_groups * tiles;
     if (grid == 0) return 0;
     if (grid > 0x7fffffff) return -1;
-    // block table of the longest request in LDS when it fits next to the
-    // 96 KB K/V ring (up to 12288 blocks = 196608 tokens)
-    int tab_cap = (a.max_seq_len + kBs - 1) / kBs;
-    if (tab_cap < 1) tab_cap = 1;
-    if (tab_cap <= kTabLdsMax) {
-      auto kern = extend_bf16_kernel<D, NW, true>;
-      const size_t lds = (size_t)tab_cap * sizeof(int32_t);
-      static bool attr_set = false;
-      if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kTabLdsMax * (int)sizeof(int32_t)) != hipSuccess)
-          return -4;
-        attr_set = true;
-      }
-      kern<<<(unsigned)grid, NW * kWave, lds, st>>>(a, tiles, units, tab_cap);
-    } else {
-      extend_bf16_kernel<D, NW, false><<<(unsigned)grid, NW * kWave, 0, st>>>(a, tiles, units,
-                                                                                  tab_cap);
-    }
+    extend_bf16_kernel<D><<<(unsigned)grid, NW * kWave, 0, st>>>(a, tiles, units);
   } else {
     if (a.max_q_len == 0) return 0;
     extend_f32_kernel<D><<<dim3(a.max_q_len, a.num_kv_heads, a.num_reqs), kWave, 0, st>>>(a);
