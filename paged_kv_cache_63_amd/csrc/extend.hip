@@ -24,11 +24,14 @@
 // copies, table lookups and the first LDS reads of the next matrix phase),
 // with a workgroup barrier after every phase, and waves 4..7 run one phase
 // behind waves 0..3.  So while one wave of a SIMD keeps its matrix core
-// busy, the other runs its exponentials on the vector ALU.  The softmax
-// uses no instruction that executes on the matrix pipeline (the bf16 dot
-// products would wait for the other wave's MFMAs), and its results are
-// pinned to the vector phase (the compiler would otherwise sink them into
-// the matrix phase that consumes them).
+// busy, the other runs its exponentials on the vector ALU; the matrix
+// phase runs at raised issue priority so that the older wave's VALU work
+// cannot starve it.  The softmax uses no instruction that executes on the
+// matrix pipeline (bf16 dot products would wait for the other wave's
+// MFMAs): row sums are taken by the matrix core itself, as products with an
+// all-ones operand.  The probabilities are pinned to the vector phase (the
+// compiler would otherwise sink them into the matrix phase that consumes
+// them).
 //
 // LDS layouts (16-byte chunks; reads hit 64 distinct banks per 16 lanes):
 // K rows are XOR-swizzled (chunk c of row i at c ^ f(i)); each V channel
@@ -56,14 +59,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBs = 16;
 constexpr int kXcds = 8;
 
-// x combined with the value of lane l ^ 32, through the VALU (no LDS).
+// Maximum of x over lanes l and l ^ 32, through the VALU (no LDS).
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (expcnt and
@@ -186,22 +185,21 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   const int wq_min = P + min(wrow0, last_row) / g;         // smallest query position of the wave
   const int wq_max = has_rows ? P + min(wrow0 + RPW - 1, last_row) / g : -1;
 
-  // Q^T operand: lane (row c32, group G) holds channels ks*16 + G*8 .. +7.
+  // Q^T operand: lane (row c32, group G) holds channels ks*16 + G*8 .. +7
+  // (loaded after the first tile copies have been issued).
   const uint16_t* qp = (const uint16_t*)a.q;
   bf16x8 qf[KS];
   int qpos;
+  const uint16_t* qrow;
+  bool qlive;
   {
     const int rr = wrow0 + c32;
     const bool live = rr <= last_row;
     const int t = live ? rr / g : 0;
     const int j = live ? rr - (rr / g) * g : 0;
     qpos = P + (live ? t : last_row / g);
-    const uint16_t* qrow = qp + ((int64_t)(q0 + t) * hq + h * g + j) * D + G * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
-      qf[ks] = live ? v : bf16x8{};
-    }
+    qrow = qp + ((int64_t)(q0 + t) * hq + h * g + j) * D + G * 8;
+    qlive = live;
   }
 
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
@@ -273,7 +271,12 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   const uint32_t voff = (uint32_t)(TILEB + c32 * 32 + ((G ^ (((c32 >> 2) ^ (c32 >> 3)) & 1)) * 16));
 
   const float c2 = a.scale * kLog2e;   // scores -> base-2 exponent units
-  float m_ref = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY;
+  f32x16 lsum;   // every value: the row sum of the lane's row
+#pragma unroll
+  for (int v = 0; v < 16; ++v) lsum[v] = 0.f;
+  const bf16x8 ones8 = bf16x8{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                              (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -300,6 +303,14 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   auto pv_mfma = [&](int i, bf16x8 f) {
     o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / DT], o[i % DT], 0, 0, 0);
   };
+  // Row sums of the rounded probabilities (exactly the weights PV uses) on
+  // the matrix core: with an all-ones A operand every row of the product is
+  // the sum over the block's keys.  The vector phase then needs no adds, and
+  // no bf16 dot instructions (those run on the matrix pipeline and would
+  // wait behind the other wave's MFMAs).
+  auto sum_mfma = [&](int b) {
+    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pf[b], lsum, 0, 0, 0);
+  };
   auto qk_mfma = [&](int i, bf16x8 f) {
     sc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i / 2], sc[i % 2], 0, 0, 0);
   };
@@ -322,6 +333,10 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   // consumed by MFMA j + NPRE.
   auto pv_qk = [&](int sp, int sq) {
     constexpr int NR = NPV - NPRE + NQK;
+    // Higher issue priority while feeding the matrix core: the other wave of
+    // the SIMD (in its vector phase) would otherwise win every issue slot
+    // and delay the MFMAs whenever it is the older wave.
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 fr[NR];
 #pragma unroll
     for (int j = 0; j < NPV - NPRE; ++j) fr[j] = vread(sp, NPRE + j);
@@ -331,6 +346,8 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) pv_mfma(i, vpre[i]);
 #pragma unroll
+    for (int b = 0; b < NBT; ++b) sum_mfma(b);
+#pragma unroll
     for (int i = NPRE; i < NPV; ++i) pv_mfma(i, fr[i - NPRE]);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) qk_mfma(i, fr[NPV - NPRE + i]);
@@ -339,7 +356,8 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NPRE + NBT, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // QK alone (first tile): LA reads, then (MFMA, read) pairs.
   auto qk = [&](int sq) {
@@ -367,16 +385,23 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
         for (int v = 0; v < 16; ++v)
           if (kbase + ch * 32 + (v >> 2) * 8 + G * 4 + (v & 3) > qpos) sc[ch][v] = -INFINITY;
     }
-    float mb = fmaxf(sc[0][0], sc[0][1]);
+    // row maximum as a depth-4 tree of three-input maxima
+    auto x = [&](int i) { return sc[i >> 4][i & 15]; };
+    float m1[11];
 #pragma unroll
-    for (int v = 2; v < 32; v += 2) mb = fmaxf(fmaxf(mb, sc[v >> 4][v & 15]), sc[v >> 4][(v & 15) + 1]);
-    mb = max_halves(mb);
+    for (int i = 0; i < 10; ++i) m1[i] = fmaxf(fmaxf(x(3 * i), x(3 * i + 1)), x(3 * i + 2));
+    m1[10] = fmaxf(x(30), x(31));
+    const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]);
+    const float m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+    const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]);
+    const float m2d = fmaxf(m1[9], m1[10]);
+    const float mb = max_halves(fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d)));
     const float m_new = mb * c2;
     const bool grow = m_new > m_ref + kLazy;
     if (__any(grow)) {   // rare after the first tile
       const float target = grow ? m_new : m_ref;
       const float alpha = __builtin_amdgcn_exp2f(m_ref - target);
-      l_run *= alpha;
+      lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m_ref = target;
@@ -389,16 +414,11 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
       for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[b >> 1][(b & 1) * 8 + e], c2, nm));
       pf[b] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                      (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-      // Row sum in fp32 adds (of the unrounded probabilities): the bf16 dot
-      // instructions would run on the matrix pipeline and stall behind the
-      // other wave's MFMAs.
-      l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     }
     // The probabilities are computed in this (vector) phase, not in the
     // matrix phase that consumes them.
 #pragma unroll
     for (int b = 0; b < NBT; ++b) materialize(pf[b]);
-    materialize(l_run);
   };
 
   // PV alone (the last tile of the workgroup).  V^T operand of block b,
@@ -431,6 +451,8 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
     }
 #pragma unroll
     for (int i = 0; i < NPV; ++i) pv_mfma(i, fr[i]);
+#pragma unroll
+    for (int b = 0; b < NBT; ++b) sum_mfma(b);
   };
 
   // Slots: waves 0..3 run matrix phase j in slot 2j and vector phase j in
@@ -473,14 +495,19 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
     fetch_entries(1, e1);
     fetch_entries(2, e2);
     if (ntiles > 3) fetch_entries(3, e_nxt);
-    wait_vm<0>();   // Q fragments in registers before the copies are counted
     issue(0, e0);
     if (ntiles > 1) issue(1, e1);
     if (ntiles > 2) issue(2, e2);
   }
-  if (ntiles > 2) wait_vm<2 * PER_T>();
-  else if (ntiles > 1) wait_vm<PER_T>();
-  else wait_vm<0>();
+  // Q after the first copies, so both latencies overlap; waiting for all
+  // of them (the compiler's own wait for Q would do the same) also covers
+  // tiles 0..2 before the first barrier.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+    qf[ks] = qlive ? v : bf16x8{};
+  }
+  wait_vm<0>();
   wg_barrier();
   const int lag = lead ? 0 : 1;
   if (!lead) wg_barrier();
@@ -521,7 +548,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
 
   // Normalise and store: lane (row c32, group G) holds channels
   // dt*32 + 8*(v/4) + 4*G + v%4 of its row.
-  const float l = sum_halves(l_run);
+  const float l = lsum[0];
   const int rr = wrow0 + c32;
   if (rr > last_row) return;
   const int tok = rr / g;

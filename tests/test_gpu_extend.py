@@ -69,6 +69,7 @@ def test_small_cases(gpu, dtype, R, plo, phi, nlo, nhi, hq, hkv, d):
     assert np.array_equal(words_of(st.k_pool), kp) and np.array_equal(words_of(st.v_pool), vp)
     want = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tab, e.scale, 16, dtype)
     err = np.abs(f64_of(out) - want).max()
+    print(f"extend {dtype} R={R} hq={hq} hkv={hkv} d={d}: max |err| {err:.3e}")
     assert err <= TOL[dtype], err
 
 
@@ -91,6 +92,7 @@ def test_multiturn_full_size_sampled(gpu):
     for r in reqs:
         a, b = int(e.cu_new[r]), int(e.cu_new[r + 1])
         err = np.abs(got[a:b, [0, 29]] - want[a:b, [0, 29]]).max()
+        print(f"multiturn request {r}: max |err| {err:.3e}")
         assert err <= 2e-2, (r, err)
 
 
@@ -121,3 +123,23 @@ def test_zero_prefix_is_causal_self_attention(gpu):
     kp, vp, tab, _, _ = P.extend_state(e)
     want = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tab, e.scale, 16, "bf16")
     assert np.abs(out - want).max() <= 2e-2
+
+
+@pytest.mark.parametrize("factor", [40.0, -25.0])
+def test_large_logits(gpu, factor):
+    """Queries scaled so that row maxima reach hundreds of base-2 exponent
+    units (and, with a negative factor, whole rows sit far below zero): the
+    running reference of the online softmax must follow them without
+    overflow or underflow."""
+    from workloads.synth import bf16_words
+    e = extend_case(721, 3, 100, 700, 30, 150, 16, 4, 128, "bf16")
+    qf = (e.q.astype(np.uint32) << np.uint32(16)).view(np.float32) * np.float32(factor)
+    e.q[...] = bf16_words(qf)
+    st = LibExtendState(e)
+    out = f64_of(st.extend())
+    kp, vp, tab, _, _ = P.extend_state(e)
+    want = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tab, e.scale, 16, "bf16")
+    assert np.isfinite(out).all()
+    err = np.abs(out - want).max()
+    print(f"large logits x{factor}: max |err| {err:.3e}")
+    assert err <= 2e-2, err
