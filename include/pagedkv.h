@@ -35,7 +35,11 @@
  *            -- a key vector is one contiguous row.
  *    v_pool  [num_blocks][num_kv_heads][head_dim][block_size]
  *            -- values are stored transposed inside a block: one row of
- *               block_size tokens per channel.
+ *               block_size tokens per channel, in which the token at
+ *               offset `off` sits at position v_pos(off) = off with bits
+ *               2 and 3 exchanged (order 0-3, 8-11, 4-7, 12-15; the map is
+ *               its own inverse).  This is the order in which the matrix
+ *               cores consume a block's tokens, two 8-byte halves per lane.
  *  A slot is phys_block * block_size + offset_in_block.
  *
  * Safety: kernels never touch memory outside the ranges the arguments
