@@ -112,10 +112,10 @@ int copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks,
                 int32_t dtype, void* stream);
 
 /*
- * Size in bytes of the fp32 workspace paged_attention_decode needs for these
- * arguments (0 when every context fits one partition).  partition_size as in
- * paged_attention_decode (0 = the library's choice).  Returns 0 for invalid
- * arguments as well; the decode call reports those.
+ * Size in bytes of the workspace paged_attention_decode needs for these
+ * arguments; partition_size as in paged_attention_decode (0 = the library's
+ * choice).  Returns 0 only for invalid arguments (the decode call reports
+ * those).
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim,
@@ -129,10 +129,11 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  * Passage: the attention kernel walks the block table and gathers the
  * sequence's physical blocks; the result equals attention over the same
  * tokens stored contiguously (Triptych page, technical summary, "The story",
- * "The surprising detail").  Long contexts are split into partitions along
- * the sequence that run in parallel and are merged afterwards ("RadixAttention:
- * Tree-Based KV Cache Reuse in SGLang Guide", section "3. Integrating
- * FlashInfer for Sub-Millisecond Paged Kernel Lookups", split-KV decode).
+ * "The surprising detail").  Contexts are split along the sequence into
+ * pieces computed in parallel and merged by the log-sum-exp rule
+ * ("RadixAttention: Tree-Based KV Cache Reuse in SGLang Guide", section "3.
+ * Integrating FlashInfer for Sub-Millisecond Paged Kernel Lookups",
+ * split-KV decode).
  *
  *   out            [num_seqs][num_q_heads][head_dim]  (dtype), written
  *   q              [num_seqs][num_q_heads][head_dim]  (dtype)
@@ -140,19 +141,33 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *                  0 .. ceil(context_lens[s]/block_size)-1 are read
  *   context_lens   [num_seqs] int32, tokens in each context (the decoded
  *                  token's own key/value included); 0 gives a zero row
- *   max_context_len  host-side upper bound of context_lens (sizes the grid;
- *                  contexts longer than it are cut to it)
+ *   max_context_len  host-side upper bound of context_lens (sizes the
+ *                  workspace; contexts longer than it are cut to it)
  *   scale          softmax scale applied to q.k
- *   partition_size tokens per split-KV partition, a multiple of block_size,
- *                  or 0 for the library's choice
- *   workspace      fp32 scratch of at least
- *                  paged_attention_decode_workspace_size(...) bytes (may be
- *                  NULL when that size is 0).  Layout, P = number of
- *                  partitions of max_context_len:
- *                    o_part [num_seqs][num_q_heads][P][head_dim]
- *                    m_part [num_seqs][num_q_heads][P]  max scaled score
- *                    l_part [num_seqs][num_q_heads][P]  sum exp(score - m)
- *                  where o_part is the partition's normalised output.
+ *   partition_size the smallest piece of a context computed on its own
+ *                  (tokens, a multiple of block_size; 0 = 512).  bf16: the
+ *                  call's (sequence, KV head, block) triples, sequence-major,
+ *                  are dealt in equal contiguous ranges of
+ *                  C = max(partition_size / block_size, ceil(total / W))
+ *                  blocks to W = 2 x (compute units) workgroups; a (sequence,
+ *                  KV head) that meets several ranges is computed in pieces
+ *                  and merged by the piece that finishes last.  fp32: fixed
+ *                  partitions of partition_size tokens, then a merge pass.
+ *   workspace      device memory of at least
+ *                  paged_attention_decode_workspace_size(...) bytes, owned
+ *                  by the caller, any contents (the call clears its
+ *                  counters first).  Layout, P = ceil(max_context_len /
+ *                  partition_size) + 1 pieces per context:
+ *                    o_part [num_seqs][num_q_heads][P][head_dim]  fp32, a
+ *                                                  piece's normalised output
+ *                    m_part [num_seqs][num_q_heads][P]  fp32, max scaled score
+ *                    l_part [num_seqs][num_q_heads][P]  fp32, sum exp(score - m)
+ *                    counters [num_seqs][num_kv_heads]  int32, pieces arrived
+ *                  Piece k of a context is the k-th range it meets.  Calls
+ *                  that share a workspace must not overlap in time.
+ *                  Returns PKV_ERR_UNSUPPORTED (bf16) when one merge's
+ *                  weights, 2 x group x P + group fp32 words, exceed the LDS
+ *                  (160 KB): a larger partition_size lowers P.
  *
  * out[s][j] = sum_t softmax_t(scale * q[s][j] . k_t) v_t over t < context_lens[s],
  * with k_t, v_t from KV head j / (num_q_heads/num_kv_heads).  Arithmetic:

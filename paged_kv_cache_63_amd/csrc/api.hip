@@ -44,24 +44,35 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
   return PKV_OK;
 }
 
-constexpr int32_t kMaxPartitionTokens = 4096;  // 256 blocks: one table entry per lane of a wave
-constexpr int32_t kMaxPartitions = 16384;      // partitions per sequence (grid y)
+constexpr int32_t kDefaultPieceTokens = 512;
+constexpr int32_t kMaxPieces = 1 << 20;      // pieces per (sequence, query head)
 
-// Library's partition choice: the largest of 1024 / 512 / 256 tokens that
-// still gives at least 1024 (sequence, KV head, partition) work items, so
-// every compute unit gets several; long partitions amortise each
-// workgroup's start-up (table and first K/V fetch).
-int32_t choose_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
-                         int32_t max_context_len) {
-  if (partition_size > 0) return partition_size;
-  const int64_t pairs = (int64_t)num_seqs * (num_kv_heads > 0 ? num_kv_heads : 1);
-  for (int32_t t = 1024; t > 256; t /= 2)
-    if (pairs * ((max_context_len + t - 1) / t) >= 1024) return t;
-  return 256;
+// Smallest piece of a context one workgroup computes (tokens): the caller's
+// choice or 512.  Longer contexts are split further only as the balance of
+// the call requires.
+int32_t choose_piece(int32_t partition_size) {
+  return partition_size > 0 ? partition_size : kDefaultPieceTokens;
 }
 
-int32_t num_partitions(int32_t max_context_len, int32_t ptok) {
-  return max_context_len <= 0 ? 1 : (max_context_len + ptok - 1) / ptok;
+// Pieces per (sequence, query head) the workspace must hold: a context of
+// nb blocks meets at most ceil(nb / piece) + 1 workgroup ranges.
+int64_t max_pieces(int32_t max_context_len, int32_t ptok) {
+  const int64_t nblk_tok = max_context_len > 0 ? max_context_len : 0;
+  return (nblk_tok + ptok - 1) / ptok + 1;
+}
+
+// Two workgroups per compute unit: what the bf16 decode kernel keeps
+// resident at once (cached per device).
+int decode_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64 && cached[dev]) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < 64) cached[dev] = 2 * cus;
+  return 2 * cus;
 }
 
 }  // namespace
@@ -119,12 +130,13 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim,
                                              int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  const int32_t ptok = choose_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0)
+    return 0;
+  const int32_t ptok = choose_piece(partition_size);
   if (ptok <= 0) return 0;
-  const int64_t P = num_partitions(max_context_len, ptok);
-  if (P <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
+  const int64_t P = max_pieces(max_context_len, ptok);
+  return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float) +
+         (size_t)num_seqs * num_kv_heads * sizeof(int32_t);
 }
 
 int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -144,17 +156,22 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID, "null pointer argument");
   if ((int64_t)num_seqs * num_kv_heads > INT32_MAX) return fail(PKV_ERR_INVALID, "too many sequences");
-  const int32_t ptok = choose_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
-  if (ptok % block_size || ptok > kMaxPartitionTokens)
-    return fail(PKV_ERR_INVALID, "partition_size %d must be a multiple of %d and <= %d",
-                partition_size, block_size, kMaxPartitionTokens);
-  const int32_t P = num_partitions(max_context_len, ptok);
-  if (P > kMaxPartitions || P > 65535)
-    return fail(PKV_ERR_INVALID, "max_context_len %d needs %d partitions (> %d)", max_context_len, P,
-                kMaxPartitions);
+  const int32_t ptok = choose_piece(partition_size);
+  if (ptok < 0 || ptok % block_size)
+    return fail(PKV_ERR_INVALID, "partition_size %d must be a multiple of %d", partition_size,
+                block_size);
+  const int64_t P = max_pieces(max_context_len, ptok);
+  if (P > kMaxPieces || (dtype == 0 && P - 1 > 65535))
+    return fail(PKV_ERR_INVALID, "max_context_len %d needs %lld pieces per context (too many)",
+                max_context_len, (long long)P);
+  // a merge stages [2][group][P] + [group] fp32 weights in LDS (160 KB)
+  if (dtype == 1 && (2 * (num_q_heads / num_kv_heads) * P + 16) * 4 > 160 * 1024 - 256)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "max_context_len %d over partition_size %d gives %lld pieces per context; use a "
+                "larger partition_size", max_context_len, ptok, (long long)P);
   const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
                                                             head_dim, max_context_len, ptok);
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  if (!workspace || workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
 
   pkv::DecodeArgs a{};
@@ -164,12 +181,13 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  if (P > 1) {
+  {
     float* ws = (float*)workspace;
     const int64_t rows = (int64_t)num_seqs * num_q_heads * P;
     a.part_o = ws;
     a.part_m = ws + rows * head_dim;
     a.part_l = a.part_m + rows;
+    a.counters = (int32_t*)(a.part_l + rows);
   }
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -178,7 +196,8 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.partition_blocks = ptok / block_size;
-  a.max_partitions = P;
+  a.max_partitions = (int32_t)P;
+  a.num_workgroups = decode_workgroups();
   a.scale = scale;
   rc = pkv::launch_decode(a, dtype, (hipStream_t)stream);
   return rc ? fail(rc, "decode launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();

@@ -64,14 +64,16 @@ struct DecodeArgs {
   float* part_o;   // [S][Hq][P][D]
   float* part_m;   // [S][Hq][P]
   float* part_l;   // [S][Hq][P]
+  int32_t* counters;  // [S][Hkv] pieces arrived per unit (zero between calls)
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t partition_blocks;  // blocks per split-KV partition
-  int32_t max_partitions;    // P
+  int32_t partition_blocks;  // smallest piece (bf16) / partition (fp32), in blocks
+  int32_t max_partitions;    // P: pieces per (sequence, query head) the workspace holds
+  int32_t num_workgroups;    // bf16 grid
   float scale;
 };
 

@@ -1,29 +1,13 @@
 // Paged decode attention for gfx950: one query token per sequence against
-// its whole paged context, split along the sequence into partitions that run
-// as separate workgroups, then merged with the log-sum-exp rule.
+// its whole paged context.
 //
-// Pass 1 (one workgroup per sequence x KV head x partition)
-//   bf16: four waves; each wave takes every fourth block of the partition.
-//     Per 16-token block the wave issues two matrix-core products:
-//       S^T[16 tok x 16 heads] = K[16 tok x D] . Q^T[D x 16 heads]
-//            (v_mfma_f32_16x16x32_bf16, D/32 of them)
-//       O^T[D x 16 heads]     += V^T[D x 16 tok] . P^T[16 tok x 16 heads]
-//            (v_mfma_f32_16x16x16_bf16, D/16 of them)
-//     The query heads that share the KV head (the GQA group, g <= 16) fill
-//     the 16 columns, so one read of a K/V block serves the whole group.
-//     The score tile comes out of the first product in exactly the register
-//     layout the second product wants for P^T (lane = head column, four
-//     consecutive tokens per lane), and V is stored transposed in the pool
-//     (channel-major inside a block), so the V^T operand is a plain
-//     coalesced 8-byte load per lane: no LDS staging, no shuffles.
-//     Online softmax (running max / sum per head) lives in registers; the
-//     per-block max needs two cross-lane steps.  Block-table entries of the
-//     partition are fetched up front, one per lane, and the next block's K/V
-//     loads are issued before the current block is computed.
-//   fp32: a plain vector-ALU kernel (one wave per workgroup) with the same
-//     partition structure and exact expf; it exists for fp32 inputs.
-// Pass 2 (one workgroup per sequence x query head, only when a sequence has
-//   more than one partition): out = sum_p o_p l_p e^(m_p-M) / sum_p l_p e^(m_p-M).
+// bf16: one kernel.  The call's K/V blocks are dealt out in equal contiguous
+// ranges to a fixed grid of workgroups; a (sequence, KV head) unit that
+// straddles ranges is computed in pieces and merged by its last piece
+// (log-sum-exp rule), so the merge needs no second launch.
+// fp32: a plain vector-ALU pass over fixed partitions (one wave per
+// workgroup, exact expf), then a merge pass for contexts with more than one
+// partition: out = sum_p o_p l_p e^(m_p-M) / sum_p l_p e^(m_p-M).
 #include <math.h>
 
 #include "common.h"
@@ -33,6 +17,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr size_t kDecodeLdsMax = 160 * 1024 - 256;   // dynamic LDS: a CU's 160 KB less the static part
 constexpr int kBs = 16;  // tokens per block
 
 __device__ __forceinline__ float wave_xor(float x, int mask) {
@@ -50,200 +35,362 @@ __device__ __forceinline__ int usable_len(const DecodeArgs& a, int s) {
   int L = a.context_lens[s];
   L = L < 0 ? 0 : L;
   const int cap_tab = a.max_blocks_per_seq * kBs;
-  const int cap_part = a.max_partitions * a.partition_blocks * kBs;
+  // the workspace holds max_partitions pieces per unit: at most
+  // ceil(nb / partition_blocks) + 1 of them for nb blocks
+  const int cap_part = (a.max_partitions - 1) * a.partition_blocks * kBs;
   L = L < cap_tab ? L : cap_tab;
   return L < cap_part ? L : cap_part;
 }
 
-// ---------------------------------------------------------------- bf16 pass 1
-// Workgroup = NW waves on one (sequence, KV head, partition); wave w takes
-// blocks w, w+NW, w+2NW, ... of the partition.  Each wave keeps DEPTH blocks
-// of K/V loads in flight in a ring of DEPTH+1 register buffers (indices fixed
-// by unrolling) while it computes on the oldest; the loads are non-temporal
-// (every K/V byte is read once per call).  No load is conditional: the trip
-// count is padded to a multiple of the ring size, padded slots re-read the
-// wave's last block and are computed fully masked.  Scheduling barriers keep
-// the compiler from hoisting a later block's products (and hence its load
-// wait) above the current block.
-template <int D, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * kWave) void decode_bf16_kernel(DecodeArgs a) {
+// ---------------------------------------------------------------- bf16 decode
+// Balanced split: the work of the call is the list of (sequence, KV head,
+// block) triples, sequence-major; unit (s, h) owns nb(s) = ceil(L_s / 16)
+// consecutive positions of that list.  The grid has a fixed number W of
+// workgroups (two per compute unit, the number that are resident at once)
+// and workgroup w takes positions [w*C, (w+1)*C) with
+// C = max(partition_blocks, ceil(total / W)), so every workgroup streams
+// the same number of K/V blocks and all of them finish together (a grid of
+// fixed-size partitions leaves compute units idle while ragged sequences
+// finish).  A unit that falls into one workgroup's range is finished there;
+// a unit split over several ranges is computed in pieces, each piece
+// writes its (o, m, l) to the workspace, and the piece that completes last
+// (an atomic arrival count per unit) merges them by the log-sum-exp rule.
+//
+// Per piece the NW waves take blocks b, b+NW, ... of the piece; per 16-token
+// block a wave issues two matrix-core products:
+//   S^T[16 tok x 16 heads] = K[16 tok x D] . Q^T[D x 16 heads]
+//        (v_mfma_f32_16x16x32_bf16, D/32 of them)
+//   O^T[D x 16 heads]     += V^T[D x 16 tok] . P^T[16 tok x 16 heads]
+//        (v_mfma_f32_16x16x16_bf16, D/16 of them)
+// The query heads of the GQA group (g <= 16) fill the 16 columns, so one
+// read of a K/V block serves the whole group; the score tile comes out in
+// the register layout P^T needs, and the channel-major V rows make the V^T
+// operand one 8-byte load per lane.  K/V loads are non-temporal (each byte
+// is read once per call).  Block-table entries are fetched one per lane, 64
+// blocks per wave at a time, and broadcast with readlane.
+
+// Agent-coherent store / load of a piece's statistics.
+__device__ __forceinline__ void put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum over the workgroup (all threads get the result); uses red[NW].
+template <int NW>
+__device__ __forceinline__ int64_t wg_sum(int64_t v, int64_t* red) {
+  for (int k = kWave / 2; k > 0; k >>= 1) v += __shfl_xor(v, k, kWave);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int64_t t = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += red[i];
+  return t;
+}
+
+// Inclusive prefix sum over the workgroup's threads; *total gets the sum.
+template <int NW>
+__device__ __forceinline__ int64_t wg_scan(int64_t v, int64_t* red, int64_t* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int k = 1; k < kWave; k <<= 1) {
+    const int64_t u = __shfl_up(v, k, kWave);
+    if (lane >= k) v += u;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    if (i < (int)(threadIdx.x / kWave)) before += red[i];
+    all += red[i];
+  }
+  *total = all;
+  return v + before;
+}
+
+// At most 128 VGPRs (four waves per SIMD): two workgroups per compute unit
+// stay resident, the number the grid is sized for.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int64_t red[NW];
+  __shared__ int64_t sh_first_g;
+  __shared__ int sh_first_s;
+  __shared__ int sh_lastv[2];
   constexpr int KQ = D / 32;  // QK products per block
   constexpr int KV = D / 16;  // PV products per block
-  constexpr int NBUF = DEPTH + 1;
+  constexpr int NT = NW * kWave;
   const int hkv = a.num_kv_heads;
   const int hq = a.num_q_heads;
   const int g = hq / hkv;
-  const int s = blockIdx.x / hkv;
-  const int h = blockIdx.x - s * hkv;
-  const int part = blockIdx.y;
-  const int L = usable_len(a, s);
-  const int ptok = a.partition_blocks * kBs;
-  const int n_part = (L + ptok - 1) / ptok;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int S = a.num_seqs;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int col = lane & 15;  // head column (B/C operands) or token/channel row (A operand)
   const int grp = lane >> 4;  // k-group of the lane
+  const int W = gridDim.x;
+  const int w = blockIdx.x;
   uint16_t* out = (uint16_t*)a.out;
+  auto nblocks = [&](int s) { return (usable_len(a, s) + kBs - 1) / kBs; };
 
-  if (L == 0) {  // empty context: a zero row (written by the first partition only)
-    if (part == 0)
-      for (int i = threadIdx.x; i < g * D; i += NW * kWave)
-        out[((int64_t)s * hq + h * g) * D + i] = 0;
-    return;
+  // Plan, part 1: total work; empty contexts get a zero row (workgroup
+  // s mod W writes it).
+  int64_t mine = 0;
+  for (int s = tid; s < S; s += NT) {
+    const int nb = nblocks(s);
+    mine += nb;
+    if (nb == 0 && s % W == w)
+      for (int i = 0; i < hq * D; ++i) out[(int64_t)s * hq * D + i] = 0;
   }
-  if (part >= n_part) return;
+  const int64_t total = (int64_t)hkv * wg_sum<NW>(mine, red);
+  const int64_t C = max((int64_t)a.partition_blocks, (total + W - 1) / W);
+  const int64_t lo = (int64_t)w * C;
+  if (lo >= total) return;
+  const int64_t hi = min(lo + C, total);
 
-  const int nblk = (L + kBs - 1) / kBs;
-  const int b0 = part * a.partition_blocks;
-  const int b1 = min(b0 + a.partition_blocks, nblk);
-  const int my_cnt = (b1 - b0 - wave + NW - 1) / NW;  // blocks this wave handles (may be <= 0)
-
-  // Block-table entries for this wave's blocks, one per lane.
-  const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  int my_entry = 0;
-  if (lane < my_cnt) my_entry = clamp_block(trow[b0 + wave + lane * NW], a.num_blocks);
-
-  // Q^T operand: lane (head column col, group grp) holds 8 channels per product.
-  const uint16_t* qp = (const uint16_t*)a.q;
-  bf16x8 qf[KQ];
-  {
-    const bool live = col < g;
-    const uint16_t* qrow = qp + ((int64_t)s * hq + h * g + (live ? col : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + grp * 8);
-      qf[kk] = live ? v : bf16x8{};
+  // Plan, part 2: the sequence whose units contain position lo (a prefix
+  // sum over the sequences, NT at a time).
+  if (tid == 0) sh_first_s = -1;
+  int64_t base = 0;
+  for (int c0 = 0; c0 < S; c0 += NT) {
+    const int s = c0 + tid;
+    const int64_t v = s < S ? (int64_t)hkv * nblocks(s) : 0;
+    int64_t chunk;
+    const int64_t incl = wg_scan<NW>(v, red, &chunk);
+    const int64_t st = base + incl - v;
+    if (v > 0 && st <= lo && lo < st + v) {
+      sh_first_s = s;
+      sh_first_g = st;
     }
+    __syncthreads();
+    if (sh_first_s >= 0) break;
+    base += chunk;
   }
+  int s = sh_first_s;
+  int64_t G = sh_first_g;
 
+  const uint16_t* qp = (const uint16_t*)a.q;
   const uint16_t* kpool = (const uint16_t*)a.k_pool;
   const uint16_t* vpool = (const uint16_t*)a.v_pool;
   const int64_t head_elems = (int64_t)kBs * D;  // one (block, head) slab
   const float sl2 = a.scale * kLog2e;
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 o[KV];
-#pragma unroll
-  for (int m = 0; m < KV; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  bf16x8 kb[NBUF][KQ];
-  u32x2 vb[NBUF][KV];
-  auto load = [&](int i, bf16x8* kd, u32x2* vd) {
-    const int phys = __builtin_amdgcn_readlane(my_entry, i);
-    const int64_t base = ((int64_t)phys * hkv + h) * head_elems;
-    const uint16_t* kr = kpool + base + col * D + grp * 8;    // token row = col
-    // channel row = col; tokens 4grp..4grp+3 sit at v_pos(4grp)
-    const uint16_t* vr = vpool + base + col * kBs + v_pos(grp * 4);
-#pragma unroll
-    for (int kk = 0; kk < KQ; ++kk)
-      kd[kk] = __builtin_bit_cast(
-          bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + kk * 32)));
-#pragma unroll
-    for (int m = 0; m < KV; ++m)
-      vd[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vr + m * 16 * kBs));
-  };
-  auto compute = [&](int i, const bf16x8* kd, const u32x2* vd) {
-    // tokens of this block inside the context; 0 for a padded slot
-    const int nvalid = i < my_cnt ? L - (b0 + wave + i * NW) * kBs : 0;
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KQ; ++kk)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kd[kk], qf[kk], sc, 0, 0, 0);
-    float z[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = (grp * 4 + r < nvalid) ? sc[r] * sl2 : -INFINITY;
-    float mb = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mb = fmaxf(mb, wave_xor(mb, 16));
-    mb = fmaxf(mb, wave_xor(mb, 32));
-    // a padded slot leaves every value as it is (its mb is -inf)
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = exp2f(m_run - m_new);
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = exp2f(z[r] - m_new);
-    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int m = 0; m < KV; ++m) o[m] *= alpha;
-    // Tail tokens of a partly filled block hold arbitrary bits (possibly
-    // NaN); p is 0 there but 0 * NaN is not, so clear those value words.
-    const int t0 = grp * 4;
-    const uint32_t mx = (t0 + 0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
-    const uint32_t my = (t0 + 2 < nvalid ? 0x0000ffffu : 0u) | (t0 + 3 < nvalid ? 0xffff0000u : 0u);
-    const bf16x4 pf = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-#pragma unroll
-    for (int m = 0; m < KV; ++m) {
-      const u32x2 vm = u32x2{vd[m].x & mx, vd[m].y & my};
-      o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vm), pf, o[m],
-                                                       0, 0, 0);
-    }
-  };
-
-  if (my_cnt > 0) {
-    const int cnt_pad = (my_cnt + NBUF - 1) / NBUF * NBUF;
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      load(min(j, my_cnt - 1), kb[j], vb[j]);
-      __builtin_amdgcn_sched_barrier(0);  // buffers complete in ring order
-    }
-    for (int i = 0; i < cnt_pad; i += NBUF) {
-#pragma unroll
-      for (int j = 0; j < NBUF; ++j) {
-        const int bi = i + j;
-        load(min(bi + DEPTH, my_cnt - 1), kb[(j + DEPTH) % NBUF], vb[(j + DEPTH) % NBUF]);
-        compute(bi, kb[j], vb[j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-
-  // Combine the four k-groups' partial sums of the same head column.
-  l_run += wave_xor(l_run, 16);
-  l_run += wave_xor(l_run, 32);
-
-  // Merge the waves of the workgroup through LDS.
+  const int P = a.max_partitions;
   float* sm_o = smem;                  // [NW][g][D]
   float* sm_m = smem + NW * g * D;     // [NW][16]
   float* sm_l = sm_m + NW * 16;        // [NW][16]
-  if (col < g) {
-#pragma unroll
-    for (int m = 0; m < KV; ++m)
-      *reinterpret_cast<f32x4*>(&sm_o[(wave * g + col) * D + m * 16 + grp * 4]) = o[m];
-    if (grp == 0) {
-      sm_m[wave * 16 + col] = m_run;
-      sm_l[wave * 16 + col] = l_run;
-    }
-  }
-  __syncthreads();
 
-  const int P = a.max_partitions;
-  for (int idx = threadIdx.x; idx < g * D; idx += NW * kWave) {
-    const int c = idx / D;
-    const int dd = idx - c * D;
-    float M = -INFINITY;
+  // One piece: blocks [bb, be) of unit (s, h); piece k of np.
+  auto piece = [&](int s, int h, int L, int bb, int be, int k, int np) {
+    // Q^T operand: lane (head column col, group grp) holds 8 channels per product.
+    bf16x8 qf[KQ];
+    {
+      const bool live = col < g;
+      const uint16_t* qrow = qp + ((int64_t)s * hq + h * g + (live ? col : 0)) * D;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + c]);
-    float lsum = 0.f, acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = exp2f(sm_m[w * 16 + c] - M);  // 0 for a wave that saw no block
-      lsum += sm_l[w * 16 + c] * f;
-      acc += sm_o[(w * g + c) * D + dd] * f;
-    }
-    const float res = acc / lsum;
-    const int64_t row = (int64_t)s * hq + h * g + c;
-    if (n_part == 1) {
-      out[row * D + dd] = f32_to_bf16(res);
-    } else {
-      a.part_o[(row * P + part) * D + dd] = res;
-      if (dd == 0) {
-        a.part_m[row * P + part] = M * kLn2;  // back to natural-log units
-        a.part_l[row * P + part] = lsum;
+      for (int kk = 0; kk < KQ; ++kk) {
+        bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + grp * 8);
+        qf[kk] = live ? v : bf16x8{};
       }
     }
+    const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4 o[KV];
+#pragma unroll
+    for (int m = 0; m < KV; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // this wave's blocks: bb + wave + i*NW, i < cnt
+    const int cnt = (be - bb - wave + NW - 1) / NW;
+    for (int i0 = 0; i0 < cnt; i0 += kWave) {
+      const int n_here = min(kWave, cnt - i0);
+      int my_entry = 0;
+      if (lane < n_here) my_entry = clamp_block(trow[bb + wave + (i0 + lane) * NW], a.num_blocks);
+      for (int i = 0; i < n_here; ++i) {
+        const int b = bb + wave + (i0 + i) * NW;
+        const int phys = __builtin_amdgcn_readlane(my_entry, i);
+        const int64_t hb = ((int64_t)phys * hkv + h) * head_elems;
+        const uint16_t* kr = kpool + hb + col * D + grp * 8;    // token row = col
+        // channel row = col; tokens 4grp..4grp+3 sit at v_pos(4grp)
+        const uint16_t* vr = vpool + hb + col * kBs + v_pos(grp * 4);
+        bf16x8 kd[KQ];
+        u32x2 vd[KV];
+#pragma unroll
+        for (int kk = 0; kk < KQ; ++kk)
+          kd[kk] = __builtin_bit_cast(
+              bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + kk * 32)));
+#pragma unroll
+        for (int m = 0; m < KV; ++m)
+          vd[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vr + m * 16 * kBs));
+        const int nvalid = L - b * kBs;   // tokens of this block inside the context
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KQ; ++kk)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kd[kk], qf[kk], sc, 0, 0, 0);
+        float z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = (grp * 4 + r < nvalid) ? sc[r] * sl2 : -INFINITY;
+        float mb = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        mb = fmaxf(mb, wave_xor(mb, 16));
+        mb = fmaxf(mb, wave_xor(mb, 32));
+        const float m_new = fmaxf(m_run, mb);
+        const float alpha = exp2f(m_run - m_new);
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = exp2f(z[r] - m_new);
+        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m_run = m_new;
+#pragma unroll
+        for (int m = 0; m < KV; ++m) o[m] *= alpha;
+        // Tail tokens of a partly filled block hold arbitrary bits (possibly
+        // NaN); p is 0 there but 0 * NaN is not, so clear those value words.
+        const int t0 = grp * 4;
+        const uint32_t mx = (t0 + 0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
+        const uint32_t my = (t0 + 2 < nvalid ? 0x0000ffffu : 0u) | (t0 + 3 < nvalid ? 0xffff0000u : 0u);
+        const bf16x4 pf = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+#pragma unroll
+        for (int m = 0; m < KV; ++m) {
+          const u32x2 vm = u32x2{vd[m].x & mx, vd[m].y & my};
+          o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vm), pf, o[m],
+                                                           0, 0, 0);
+        }
+      }
+    }
+
+    // Combine the four k-groups' partial sums of the same head column, then
+    // the waves of the workgroup through LDS.
+    l_run += wave_xor(l_run, 16);
+    l_run += wave_xor(l_run, 32);
+    __syncthreads();   // the previous piece's readers are done with the LDS
+    if (col < g) {
+#pragma unroll
+      for (int m = 0; m < KV; ++m)
+        *reinterpret_cast<f32x4*>(&sm_o[(wave * g + col) * D + m * 16 + grp * 4]) = o[m];
+      if (grp == 0) {
+        sm_m[wave * 16 + col] = m_run;
+        sm_l[wave * 16 + col] = l_run;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < g * D; idx += NT) {
+      const int c = idx / D;
+      const int dd = idx - c * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_m[v * 16 + c]);
+      float lsum = 0.f, acc = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const float f = exp2f(sm_m[v * 16 + c] - M);  // 0 for a wave that saw no block
+        lsum += sm_l[v * 16 + c] * f;
+        acc += sm_o[(v * g + c) * D + dd] * f;
+      }
+      const int64_t row = (int64_t)s * hq + h * g + c;
+      if (np == 1) {
+        out[row * D + dd] = f32_to_bf16(acc / lsum);
+      } else {
+        put(&a.part_o[(row * P + k) * D + dd], acc / lsum);
+        if (dd == 0) {
+          put(&a.part_m[row * P + k], M * kLn2);  // natural-log units
+          put(&a.part_l[row * P + k], lsum);
+        }
+      }
+    }
+  };
+
+  // Merge all np pieces of unit (s, h) (called by the piece that arrived
+  // last): the pieces' weights l_j e^(m_j - M) go through LDS (one load per
+  // (head, piece) across the workgroup), then every (head, channel) thread
+  // sums its o_j with eight loads in flight.
+  auto merge = [&](int s, int h, int np) {
+    float* sw = smem;   // [g][np] m, [g][np] weights, [g] inverse sums
+    for (int idx = tid; idx < g * np; idx += NT) {
+      const int c = idx / np;
+      const int j = idx - c * np;
+      const int64_t row = (int64_t)s * hq + h * g + c;
+      sw[idx] = get(&a.part_m[row * P + j]);
+      sw[g * np + idx] = get(&a.part_l[row * P + j]);
+    }
+    __syncthreads();
+    if (tid < g) {
+      float M = -INFINITY;
+      for (int j = 0; j < np; ++j) M = fmaxf(M, sw[tid * np + j]);
+      float wsum = 0.f;
+      for (int j = 0; j < np; ++j) {
+        const float wt = sw[g * np + tid * np + j] * expf(sw[tid * np + j] - M);
+        sw[g * np + tid * np + j] = wt;
+        wsum += wt;
+      }
+      sw[2 * g * np + tid] = 1.f / wsum;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < g * D; idx += NT) {
+      const int c = idx / D;
+      const int dd = idx - c * D;
+      const int64_t row = (int64_t)s * hq + h * g + c;
+      const float* wts = sw + g * np + c * np;
+      float acc = 0.f;
+      for (int j0 = 0; j0 < np; j0 += 8) {
+        float ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ov[u] = get(&a.part_o[(row * P + min(j0 + u, np - 1)) * D + dd]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < np) acc = fmaf(wts[j0 + u], ov[u], acc);
+      }
+      out[row * D + dd] = f32_to_bf16(acc * sw[2 * g * np + c]);
+    }
+    __syncthreads();   // the LDS is reused by the next merge
+  };
+
+  // Walk the units that intersect [lo, hi).  Only the first and the last
+  // of them can be split (the others lie wholly inside the range), so at
+  // most two pieces wait to be published.
+  int n_pend = 0;
+  int pend_s[2] = {0, 0}, pend_h[2] = {0, 0}, pend_np[2] = {0, 0};
+  while (G < hi && s < S) {
+    const int L = usable_len(a, s);
+    const int nb = (L + kBs - 1) / kBs;
+    for (int h = 0; h < hkv; ++h) {
+      const int64_t Gh = G + (int64_t)h * nb;
+      const int64_t a0 = max(lo, Gh), a1 = min(hi, Gh + nb);
+      if (a0 < a1) {
+        const int k = (int)(w - Gh / C);
+        const int np = (int)((Gh + nb - 1) / C - Gh / C + 1);
+        piece(s, h, L, (int)(a0 - Gh), (int)(a1 - Gh), k, np);
+        if (np > 1 && n_pend < 2) {
+          pend_s[n_pend] = s;
+          pend_h[n_pend] = h;
+          pend_np[n_pend] = np;
+          ++n_pend;
+        }
+      }
+    }
+    G += (int64_t)hkv * nb;
+    ++s;
   }
+  if (n_pend == 0) return;
+
+  // Publish this workgroup's split pieces (once, at the end, so that the
+  // stores have long completed); the piece of a unit that arrives last
+  // merges the unit.  Pieces are written and read with agent-coherent
+  // accesses (they write through, and read past, the per-XCD L2 caches,
+  // which are not coherent with one another), every thread's stores are
+  // complete before the workgroup counts itself in, and the arrival count is
+  // an atomic add: no cache-wide fence is needed.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid < n_pend) {
+    int32_t* arrivals = &a.counters[(int64_t)pend_s[tid] * hkv + pend_h[tid]];
+    const int prev = __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_lastv[tid] = prev == pend_np[tid] - 1;
+  }
+  __syncthreads();
+  for (int i = 0; i < n_pend; ++i)
+    if (sh_lastv[i]) merge(pend_s[i], pend_h[i], pend_np[i]);
 }
 
 // ---------------------------------------------------------------- fp32 pass 1
@@ -408,25 +555,44 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 
+// Clears the arrival counters before the decode kernel counts into them
+// (a kernel rather than a memset, so the call can be captured in a graph).
+__global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* c, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) c[i] = 0;
+}
+
 template <int D>
 int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
-  const dim3 grid(a.num_seqs * a.num_kv_heads, a.max_partitions);
   const int g = a.num_q_heads / a.num_kv_heads;
   if (dtype == 1) {
-    // 8 waves per workgroup, no register prefetch (4 waves per SIMD resident):
-    // the fastest of the depth / width combinations measured on MI355X.
     constexpr int NW = 8;
-    const size_t lds = (size_t)(NW * g * D + 2 * NW * 16) * sizeof(float);
-    decode_bf16_kernel<D, NW, 0><<<grid, NW * kWave, lds, st>>>(a);
-  } else {
-    decode_f32_kernel<D><<<grid, kWave, 0, st>>>(a);
+    // wave-merge area [NW][g][D] + [NW][16] m + [NW][16] l, also used for
+    // the piece weights of a merge ([2][g][P] + [g])
+    const size_t words = (size_t)max(NW * g * D + 2 * NW * 16, 2 * g * a.max_partitions + g);
+    const size_t lds = words * sizeof(float);
+    if (lds > kDecodeLdsMax) return -2;
+    auto kern = decode_bf16_kernel<D, NW>;
+    static bool attr_set = false;   // dynamic LDS above 64 KB needs the limit raised once
+    if (!attr_set) {
+      if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kDecodeLdsMax) != hipSuccess)
+        return -4;
+      attr_set = true;
+    }
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t cgrid = (units + 255) / 256;
+    clear_counters_kernel<<<(int)(cgrid < 1024 ? (cgrid > 0 ? cgrid : 1) : 1024), 256, 0, st>>>(a.counters, units);
+    kern<<<a.num_workgroups, NW * kWave, lds, st>>>(a);
+    return status_of(hipGetLastError());
   }
+  const int n_part = a.max_partitions - 1;   // fixed partitions of the fp32 path
+  const dim3 grid(a.num_seqs * a.num_kv_heads, n_part);
+  decode_f32_kernel<D><<<grid, kWave, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return -4;
-  if (a.max_partitions > 1) {
+  if (n_part > 1) {
     const dim3 mgrid(a.num_q_heads, a.num_seqs);
-    if (dtype == 1) decode_merge_kernel<D, true><<<mgrid, kWave, 0, st>>>(a);
-    else decode_merge_kernel<D, false><<<mgrid, kWave, 0, st>>>(a);
+    decode_merge_kernel<D, false><<<mgrid, kWave, 0, st>>>(a);
     e = hipGetLastError();
   }
   return status_of(e);

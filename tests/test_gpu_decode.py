@@ -10,6 +10,7 @@ import torch
 import oracle_pins as P
 from gpu_helpers import LibDecodeState, f64_of, i32, words_of
 from oracle import attention, numerics, paging
+from paged_kv_cache_63_amd import _lib
 from workloads import decode_case, gqa4_decode, long_context_decode, tiny_fp32_decode
 
 pytestmark = pytest.mark.gpu
@@ -80,31 +81,66 @@ def test_long_context_full_size_sampled(gpu):
             assert err <= 2e-2, (s, h, err)
 
 
-def test_partials_match_oracle_partitions(gpu):
-    """Pass-1 workspace: each partition's (o_p, m_p, l_p) against the
-    oracle's split-KV pieces."""
+def decode_plan(lens, hkv, piece_tokens, workgroups):
+    """The bf16 kernel's split of the call, as the header documents it:
+    positions are (sequence, KV head, block) triples, sequence-major;
+    workgroup w takes [w*C, (w+1)*C) with C = max(piece blocks,
+    ceil(total / W)).  Yields (s, h, k, np, first block, end block) for every
+    piece of a unit that is split (np > 1)."""
+    nb = [-(-int(L) // 16) for L in lens]
+    total = hkv * sum(nb)
+    C = max(piece_tokens // 16, -(-total // workgroups))
+    G = 0
+    for s, n in enumerate(nb):
+        for h in range(hkv):
+            Gh = G + h * n
+            if n == 0:
+                continue
+            w0, w1 = Gh // C, (Gh + n - 1) // C
+            for w in range(w0, w1 + 1):
+                a0, a1 = max(w * C, Gh), min((w + 1) * C, Gh + n)
+                yield s, h, w - w0, w1 - w0 + 1, a0 - Gh, a1 - Gh
+        G += hkv * n
+
+
+def test_partials_match_oracle_pieces(gpu):
+    """Workspace after a call: each piece (o_p, m_p, l_p) of every split
+    unit against the oracle's statistics over the same tokens, and each
+    unit's arrival count equal to its number of pieces."""
     case = decode_case(301, 3, 700, 1500, 16, 4, 128, "bf16")
     st = LibDecodeState(case)
-    ptok = 256
+    ptok = 64
     out, ws = st.decode(partition_size=ptok)
     torch.cuda.synchronize()
-    S, hq, d = case.num_seqs, case.num_q_heads, case.head_dim
-    Pm = -(-int(max(case.context_lens)) // ptok)
-    w = ws.view(torch.float32).cpu().numpy().astype(np.float64)
-    rows = S * hq * Pm
-    o = w[:rows * d].reshape(S, hq, Pm, d)
-    m = w[rows * d:rows * (d + 1)].reshape(S, hq, Pm)
-    l = w[rows * (d + 1):rows * (d + 2)].reshape(S, hq, Pm)
-    for s in range(S):
+    S, hq, hkv, d = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
+    g = hq // hkv
+    P = -(-int(max(case.context_lens)) // ptok) + 1
+    raw = ws.cpu().numpy()
+    rows = S * hq * P
+    w = raw[:rows * (d + 2) * 4].view(np.float32).astype(np.float64)
+    o = w[:rows * d].reshape(S, hq, P, d)
+    m = w[rows * d:rows * (d + 1)].reshape(S, hq, P)
+    l = w[rows * (d + 1):rows * (d + 2)].reshape(S, hq, P)
+    counters = raw[rows * (d + 2) * 4:rows * (d + 2) * 4 + S * hkv * 4].view(np.int32)
+    expect = np.zeros(S * hkv, np.int64)
+    wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    checked = 0
+    for s, h, k, np_, b0, b1 in decode_plan(case.context_lens, hkv, ptok, wg):
         c0, c1 = case.cu_tokens[s], case.cu_tokens[s + 1]
+        t0, t1 = 16 * b0, min(16 * b1, c1 - c0)
         oo, mm, ll = attention.partition_partials(numerics.to_f64(case.q[s], "bf16"),
-                                                  numerics.to_f64(case.k[c0:c1], "bf16"),
-                                                  numerics.to_f64(case.v[c0:c1], "bf16"),
-                                                  case.scale, ptok)
-        n = oo.shape[0]
-        assert np.abs(o[s, :, :n].transpose(1, 0, 2) - oo).max() <= 2e-2
-        assert np.abs(m[s, :, :n].T - mm).max() <= 2e-2
-        assert (np.abs(l[s, :, :n].T - ll) / ll).max() <= 2e-2
+                                                  numerics.to_f64(case.k[c0 + t0:c0 + t1], "bf16"),
+                                                  numerics.to_f64(case.v[c0 + t0:c0 + t1], "bf16"),
+                                                  case.scale, t1 - t0)
+        heads = slice(h * g, (h + 1) * g)
+        assert np.abs(o[s, heads, k] - oo[0, heads]).max() <= 2e-2
+        assert np.abs(m[s, heads, k] - mm[0, heads]).max() <= 2e-2
+        assert (np.abs(l[s, heads, k] - ll[0, heads]) / ll[0, heads]).max() <= 2e-2
+        if k == 0:
+            expect[s * hkv + h] = np_
+        checked += 1
+    assert checked > 0
+    assert np.array_equal(counters, expect)
 
 
 def test_permutation_bit_identical(gpu):
@@ -157,3 +193,21 @@ def test_context_longer_than_declared_max_is_cut_not_overrun(gpu):
     kp, vp, tab = P.oracle_pools_for_decode(cut)
     want = attention.decode(cut.q, kp, vp, tab, np.array([128, 128]), cut.scale, 16, "bf16")
     assert np.abs(f64_of(out) - want).max() <= 2e-2
+
+
+def test_workspace_reused_across_calls(gpu):
+    """One workspace (filled with garbage first) serves consecutive calls of
+    different shapes, whose counters and pieces sit at different offsets:
+    every output matches the oracle."""
+    cases = [decode_case(811, 5, 200, 2500, 32, 8, 128, "bf16"),
+             decode_case(812, 9, 1, 900, 32, 8, 128, "bf16"),
+             decode_case(813, 2, 1500, 3000, 32, 8, 128, "bf16")]
+    need = max(_lib.paged_attention_decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                                          c.head_dim, 3000, 64) for c in cases)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for c in cases:
+            st = LibDecodeState(c)
+            out, _ = st.decode(partition_size=64, max_context_len=3000, workspace=ws)
+            err = np.abs(f64_of(out) - _oracle_out(c)).max()
+            assert err <= 2e-2, (rep, err)
