@@ -35,6 +35,17 @@ What it computes, and where each step comes from:
                        pointer change"; "PagedAttention 与 RadixAttention"
                        (khotyn.com), section "PagedAttention".
 
+* ``prefix_cache`` -- plain models of the two automatic prefix caches: one
+                       keyed by (salt, whole token prefix) for the chained-hash
+                       cache, and a radix tree kept as a flat node list searched
+                       by scanning.  Sources: "PagedAttention and
+                       RadixAttention: Let's Talk About KV Cache", sections
+                       "RadixAttention: A Tree That Does Not Forget", "Two
+                       Layers, Not Two Rivals" and "Beyond the Two Techniques";
+                       "RadixAttention: Tree-Based KV Cache Reuse in SGLang
+                       Guide", "Architecture"; "PagedAttention 与
+                       RadixAttention", section "RadixAttention".
+
 Numerics: float64 throughout.  bf16 inputs are widened exactly (bits << 16 as
 float32, then float64); float32 inputs are widened exactly.
 
@@ -44,4 +55,4 @@ invariants the pages state (see ``tests/test_oracle_pins.py``).  No function in
 this package is "parity unpinned".
 """
 
-from . import attention, block_manager, numerics, paging  # noqa: F401
+from . import attention, block_manager, numerics, paging, prefix_cache  # noqa: F401

@@ -2,6 +2,10 @@
 
 * ``allocator`` -- host-side reference-counted block manager (block tables,
   slot mappings, fork, copy-on-write pairs).
+* ``prefix_cache`` -- automatic prefix caching by chained block hashes
+  (``PrefixCachingAllocator``).
+* ``radix_cache``  -- radix-tree prefix cache with LRU leaf eviction
+  (``RadixCache``) over a ``BlockAllocator``.
 * ``_lib``      -- ctypes binding of ``libpagedkv.so``: the device calls
   ``paged_kv_append``, ``copy_blocks``, ``paged_attention_decode``,
   ``paged_attention_extend`` (+ ``paged_kv_gather``), taking torch tensors on
@@ -10,6 +14,8 @@
 """
 
 from .allocator import BlockAllocator, OutOfBlocks, kv_bytes_per_token  # noqa: F401
+from .prefix_cache import PrefixCachingAllocator, block_hash  # noqa: F401
+from .radix_cache import RadixCache  # noqa: F401
 
 
 def __getattr__(name):

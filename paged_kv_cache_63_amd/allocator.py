@@ -65,6 +65,9 @@ class BlockAllocator:
         self.nblk = np.zeros(self.max_seqs, dtype=np.int32)
         self.ref = np.zeros(self.num_blocks, dtype=np.int32)
         self.live = np.zeros(self.max_seqs, dtype=bool)
+        # A sealed block's contents are frozen (a prefix cache indexes them):
+        # a write into it copies it first, even by its only owner.
+        self.sealed = np.zeros(self.num_blocks, dtype=bool)
         order = np.arange(self.num_blocks) if free_order is None else np.asarray(free_order)
         if sorted(int(b) for b in order) != list(range(self.num_blocks)):
             raise ValueError("free_order must be a permutation of range(num_blocks)")
@@ -73,12 +76,67 @@ class BlockAllocator:
 
     # ---------------------------------------------------------------- blocks
     def _take(self, n: int) -> np.ndarray:
+        """Hand out ``n`` blocks (the caller has checked ``_available``)."""
         out = np.fromiter((self._free.popleft() for _ in range(n)), dtype=np.int32, count=n)
         self.ref[out] = 1
         return out
 
-    def num_free(self) -> int:
+    def _available(self) -> int:
+        """Blocks a request may still take."""
         return len(self._free)
+
+    def _release(self, blocks) -> None:
+        """Blocks whose count just reached zero, in logical order."""
+        self._free.extend(int(b) for b in blocks)
+
+    def _idle(self):
+        """Unreferenced blocks kept out of the free list (none here)."""
+        return ()
+
+    def num_free(self) -> int:
+        return self._available()
+
+    def incref(self, blocks) -> None:
+        """One more reference on each block (a cache holding it, a new owner).
+        Every block must already be referenced."""
+        blocks = np.asarray(blocks, dtype=np.int64)
+        if len(blocks) and (self.ref[blocks] <= 0).any():
+            raise ValueError("incref on an unreferenced block")
+        np.add.at(self.ref, blocks, 1)
+
+    def decref(self, blocks) -> int:
+        """Drop one reference from each block; blocks that reach zero are
+        released in the order given.  Returns how many were released."""
+        blocks = np.asarray(blocks, dtype=np.int64)
+        if len(blocks) and (self.ref[blocks] <= 0).any():
+            raise ValueError("decref on an unreferenced block")
+        zero = []
+        for b in blocks:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                zero.append(int(b))
+        self._release(zero)
+        return len(zero)
+
+    def adopt(self, blocks, num_tokens: int) -> int:
+        """New sequence whose first blocks are ``blocks`` (already referenced
+        elsewhere, e.g. by a prefix cache), holding ``num_tokens`` tokens.
+        Each block gains a reference."""
+        blocks = np.asarray(blocks, dtype=np.int64)
+        if num_tokens != len(blocks) * self.block_size:
+            raise ValueError("adopted blocks must be full")
+        if len(blocks) > self.max_blocks_per_seq:
+            raise ValueError("sequence would exceed max_blocks_per_seq")
+        if len(np.unique(blocks)) != len(blocks):
+            raise ValueError("a block may appear once per sequence")
+        if len(blocks) and (self.ref[blocks] <= 0).any():
+            raise ValueError("adopted blocks must be referenced")
+        sid = self.new_seq()
+        self.ref[blocks] += 1
+        self.tables[sid, :len(blocks)] = blocks
+        self.nblk[sid] = len(blocks)
+        self.lens[sid] = num_tokens
+        return sid
 
     def refcount(self, block: int) -> int:
         return int(self.ref[block])
@@ -111,18 +169,24 @@ class BlockAllocator:
         pairs = np.zeros((0, 2), dtype=np.int32)
         if n <= 0:
             return np.zeros(0, dtype=np.int32), pairs
-        cow = pos0 % B != 0 and self.ref[self.tables[sid, nb - 1]] > 1
+        last = int(self.tables[sid, nb - 1]) if nb else -1
+        cow = pos0 % B != 0 and (self.ref[last] > 1 or bool(self.sealed[last]))
         new = -(-(pos0 + n) // B) - nb
-        if int(cow) + new > len(self._free):
-            raise OutOfBlocks(f"need {int(cow) + new} blocks, {len(self._free)} free")
+        # a copied block that nobody else holds becomes available right after
+        # its copy is taken, before the new blocks are
+        gain = int(cow and self.ref[last] == 1)
+        avail = self._available()
+        if int(cow) + new > avail + gain or (cow and avail == 0):
+            raise OutOfBlocks(f"need {int(cow) + new} blocks, {avail} free")
         if nb + new > self.max_blocks_per_seq:
             raise ValueError("sequence would exceed max_blocks_per_seq")
         if cow:
-            src = int(self.tables[sid, nb - 1])
             dst = int(self._take(1)[0])
-            self.ref[src] -= 1
+            self.ref[last] -= 1
+            if self.ref[last] == 0:
+                self._release([last])
             self.tables[sid, nb - 1] = dst
-            pairs = np.array([[src, dst]], dtype=np.int32)
+            pairs = np.array([[last, dst]], dtype=np.int32)
         if new:
             self.tables[sid, nb:nb + new] = self._take(new)
             self.nblk[sid] = nb + new
@@ -148,6 +212,8 @@ class BlockAllocator:
         nb = self.nblk[sids].astype(np.int64)
         need_new = pos % B == 0
         last = np.where(need_new, 0, self.tables[sids, np.maximum(nb - 1, 0)]).astype(np.int64)
+        if self.sealed[last[~need_new]].any():
+            return self._append_step_in_turn(sids)
         shared = (~need_new) & (self.ref[last] > 1)
         cow = np.zeros(len(sids), dtype=bool)
         ref_after = {}
@@ -159,8 +225,8 @@ class BlockAllocator:
                 ref_after[b] = c - 1
         takers = need_new | cow
         k = int(takers.sum())
-        if k > len(self._free):
-            raise OutOfBlocks(f"need {k} blocks, {len(self._free)} free")
+        if k > self._available():
+            raise OutOfBlocks(f"need {k} blocks, {self._available()} free")
         if (nb[need_new] + 1 > self.max_blocks_per_seq).any():
             raise ValueError("sequence would exceed max_blocks_per_seq")
         fresh = self._take(k)
@@ -178,6 +244,30 @@ class BlockAllocator:
         slots = self.tables[sids, pos // B].astype(np.int64) * B + pos % B
         self.lens[sids] += 1
         return slots.astype(np.int32), pairs
+
+    def _append_step_in_turn(self, sids):
+        """``append_tokens(s, 1)`` for each sequence in turn; used when a step
+        writes into a sealed block, whose copy may free it part-way through
+        the step.  All-or-nothing like the batched path."""
+        saved = self._snapshot()
+        slots, pairs = [], []
+        try:
+            for s in sids:
+                sl, pr = self.append_tokens(int(s), 1)
+                slots.append(sl)
+                pairs.append(pr)
+        except (OutOfBlocks, ValueError):
+            self._restore(saved)
+            raise
+        return (np.concatenate(slots).astype(np.int32),
+                np.concatenate(pairs).astype(np.int32).reshape(-1, 2))
+
+    def _snapshot(self):
+        return (self.tables.copy(), self.lens.copy(), self.nblk.copy(), self.ref.copy(),
+                self.sealed.copy(), deque(self._free))
+
+    def _restore(self, saved):
+        self.tables, self.lens, self.nblk, self.ref, self.sealed, self._free = saved
 
     def fork(self, sid: int, n: int = 1):
         """``n`` new sequences sharing every block of ``sid`` by reference."""
@@ -206,8 +296,7 @@ class BlockAllocator:
         keep = -(-new_len // self.block_size)
         blocks = self.tables[sid, keep:nb].copy()
         self.ref[blocks] -= 1
-        for b in blocks[self.ref[blocks] == 0]:
-            self._free.append(int(b))
+        self._release(blocks[self.ref[blocks] == 0])
         self.tables[sid, keep:nb] = -1
         self.nblk[sid] = keep
         self.lens[sid] = new_len
@@ -219,8 +308,7 @@ class BlockAllocator:
         nb = int(self.nblk[sid])
         blocks = self.tables[sid, :nb].copy()
         self.ref[blocks] -= 1
-        for b in blocks[self.ref[blocks] == 0]:
-            self._free.append(int(b))
+        self._release(blocks[self.ref[blocks] == 0])
         self.tables[sid] = -1
         self.lens[sid] = 0
         self.nblk[sid] = 0
@@ -238,9 +326,13 @@ class BlockAllocator:
         """Idle slots of the sequence (all in its last block)."""
         return int(self.nblk[sid]) * self.block_size - int(self.lens[sid])
 
-    def validate(self) -> None:
-        """Check every invariant; raises AssertionError on the first breach."""
+    def validate(self, held=None) -> None:
+        """Check every invariant; raises AssertionError on the first breach.
+        ``held``: references per block held outside sequence tables (a prefix
+        tree's), if any."""
         count = np.zeros(self.num_blocks, dtype=np.int64)
+        if held is not None:
+            count += held
         for sid in np.flatnonzero(self.live):
             nb = int(self.nblk[sid])
             row = self.tables[sid, :nb]
@@ -249,8 +341,14 @@ class BlockAllocator:
             assert len(np.unique(row)) == nb, "block repeated within a sequence"
             assert 0 <= self.waste(sid) < self.block_size or nb == 0, "waste bound"
             count[row] += 1
-        assert (count == self.ref).all(), "refcount != number of references"
-        free = np.fromiter(self._free, dtype=np.int64, count=len(self._free))
+        assert (count + self._holders() == self.ref).all(), "refcount != number of references"
+        free = np.array(list(self._free) + list(self._idle()), dtype=np.int64)
         assert len(np.unique(free)) == len(free), "block twice on the free list"
         assert (self.ref[free] == 0).all(), "referenced block on the free list"
+        assert not self.sealed[np.asarray(list(self._free), dtype=np.int64)].any(), \
+            "sealed block on the free list"
         assert len(free) + int((self.ref > 0).sum()) == self.num_blocks, "block leaked"
+
+    def _holders(self) -> np.ndarray:
+        """References held outside sequence tables, per block (a cache's)."""
+        return np.zeros(self.num_blocks, dtype=np.int64)
