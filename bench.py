@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=WORKLOADS, default="gqa4-decode")
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--plain-decode", action="store_true",
+                    help="shared-prefix workload: decode every sequence on its own "
+                         "(paged_attention_decode) instead of the shared-prefix decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -352,6 +355,14 @@ def run_shared(args, case, torch, lib, alloc_cls):
     ev_pairs, snaps = [], []
     kv_per_tok = 2 * hkv * d * 2
     n_pairs = 0
+    groups = None
+    if not args.plain_decode:
+        # the shared prompt's blocks lead every table for the whole run: the
+        # groups are found once, from the tables the allocator holds
+        groups = lib.shared_prefix_groups(alloc.tables[rows], alloc.lens[rows] + 1)
+        ws = torch.empty(lib.paged_attention_decode_shared_workspace_size(
+            S, hq, hkv, d, maxb * 16, 0, len(groups[2]), groups[3], groups[4]),
+            dtype=torch.uint8, device=dev)
     for i in range(T):
         timed = i >= args.warmup
         if i == args.warmup:
@@ -369,8 +380,12 @@ def run_shared(args, case, torch, lib, alloc_cls):
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        lib.paged_attention_decode(out, q_steps[i], k_pool, v_pool, tables_d, lens_d,
-                                   int(lens.max()), case.scale, 0, ws)
+        if groups is None:
+            lib.paged_attention_decode(out, q_steps[i], k_pool, v_pool, tables_d, lens_d,
+                                       int(lens.max()), case.scale, 0, ws)
+        else:
+            lib.paged_attention_decode_shared(out, q_steps[i], k_pool, v_pool, tables_d, lens_d,
+                                              maxb * 16, case.scale, groups, 0, ws)
         if timed:
             e1.record()
             ev_pairs.append((e0, e1))
@@ -389,7 +404,7 @@ def run_shared(args, case, torch, lib, alloc_cls):
         logical.append(int(lens.sum()) * kv_per_tok)
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
     return dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=uniq, logical=logical,
-                cow_pairs=n_pairs)
+                cow_pairs=n_pairs, shared=groups is not None)
 
 
 def main():
@@ -429,7 +444,7 @@ def main():
         kern = ["extend.hip"]
     elif args.workload == "shared-prefix-decode":
         r = run_shared(args, case, torch, lib, BlockAllocator)
-        kern = ["decode.hip"]
+        kern = ["decode.hip"] if args.plain_decode else ["decode.hip", "extend.hip"]
     else:
         r = run_decode(args, case, torch, lib, BlockAllocator)
         kern = ["decode.hip"]
@@ -452,7 +467,9 @@ def main():
         achieved = per_launch / mean_dur / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "paged_attention_decode (pass 1 decode_bf16_kernel + pass 2 merge)",
+                "kernel": ("paged_attention_decode_shared (prefix pass extend_bf16_kernel<PREFIX> "
+                           "+ decode_bf16_kernel<SHARED>)" if r.get("shared") else
+                           "paged_attention_decode (decode_bf16_kernel, merge fused)"),
                 "launch_us": round(mean_dur * 1e6, 2), "bytes_per_launch": int(per_launch)}
         value = r["tokens"] / el
         unit = "tokens/s"

@@ -184,6 +184,77 @@ int paged_attention_decode(void* out, const void* q,
                            int32_t dtype, void* stream);
 
 /*
+ * Size in bytes of the workspace paged_attention_decode_shared needs for
+ * these arguments (it depends on the device's compute-unit count, which
+ * sets the prefix pass's key split).  Returns 0 for invalid arguments.
+ */
+size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_context_len, int32_t partition_size,
+                                                    int32_t num_groups, int32_t max_group_size,
+                                                    int32_t max_prefix_blocks);
+
+/*
+ * paged_attention_decode_shared -- paged_attention_decode for a batch in
+ * which groups of sequences share the leading physical blocks of their
+ * tables (a common system prompt, parallel samples forked from one parent).
+ *
+ * Passage: sharing a prefix is a pointer change, every sharer's table
+ * pointing at the same physical blocks (Triptych page, technical summary
+ * and "Look closer"); prefix caches hand the same blocks to every request
+ * that starts with the same tokens ("PagedAttention and RadixAttention:
+ * Let's Talk About KV Cache", "Two Layers, Not Two Rivals").  The pages do
+ * not describe decoding such a batch; here the attention over a shared
+ * prefix is computed once per (group, KV head) for all members' query heads
+ * together, on the matrix cores, and combined with each member's attention
+ * over the rest of its context by the log-sum-exp rule ("RadixAttention:
+ * Tree-Based KV Cache Reuse in SGLang Guide", section "3. Integrating
+ * FlashInfer ...", split-KV decode).  The result is the same function as
+ * paged_attention_decode's.
+ *
+ * Arguments as paged_attention_decode, plus (device memory unless noted):
+ *   group_offsets  [num_groups+1] int32: group i's members are
+ *                  group_seqs[group_offsets[i] .. group_offsets[i+1]-1]
+ *   group_seqs     sequence indices; a sequence belongs to at most one group
+ *   group_prefix_blocks [num_groups] int32: the number of leading table
+ *                  entries every member of the group has in common (the same
+ *                  physical block ids, read from the first member's row)
+ *   num_groups, max_group_size, max_prefix_blocks  host-side: the group
+ *                  count, the largest member count and the largest
+ *                  group_prefix_blocks (they size the prefix pass's grid)
+ *   workspace      at least paged_attention_decode_shared_workspace_size(...)
+ *                  bytes, any contents: the paged_attention_decode layout
+ *                  (o, m, l pieces and counters), then seq_prefix
+ *                  [num_seqs][2] int32 (the block each sequence's own pass
+ *                  starts at, and how many prefix partials it folds in), then
+ *                  at the next 256-byte boundary the prefix partials o
+ *                  [num_seqs][num_q_heads][NS][head_dim], m and l
+ *                  [num_seqs][num_q_heads][NS] fp32 (NS key splits).
+ *
+ * A member sees the shared blocks up to, not including, the block that holds
+ * its last token (that block is always in its own pass): its first
+ * min(prefix_blocks, (context_len - 1) / block_size) table entries must be
+ * the first member's (the call reads the prefix blocks from the first
+ * member's row only), and the first member must hold all prefix_blocks.
+ * Otherwise the result is undefined, but every access stays inside the pool.  fp32 inputs, or no
+ * groups, run paged_attention_decode unchanged.  Errors as
+ * paged_attention_decode; PKV_ERR_UNSUPPORTED when the merge weights,
+ * 2 x group x (P + NS) + group fp32 words, exceed the LDS.
+ */
+int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
+                                  const void* v_pool, int32_t num_blocks,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  float scale, const int32_t* group_offsets,
+                                  const int32_t* group_seqs, const int32_t* group_prefix_blocks,
+                                  int32_t num_groups, int32_t max_group_size,
+                                  int32_t max_prefix_blocks, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  void* stream);
+
+/*
  * paged_attention_extend -- new tokens of each request (a chunked prefill
  * after a cached prefix) attend causally to the prefix plus themselves.
  *

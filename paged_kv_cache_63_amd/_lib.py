@@ -20,7 +20,8 @@ _LIB = None
 
 PKV_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SYMBOLS = ("paged_kv_append", "copy_blocks", "paged_attention_decode_workspace_size",
-           "paged_attention_decode", "paged_attention_extend", "paged_kv_gather",
+           "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
+           "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
            "paged_kv_last_error")
 
 
@@ -49,6 +50,12 @@ def load():
     lib.paged_attention_decode.restype = ctypes.c_int
     lib.paged_attention_decode.argtypes = [p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32,
                                            i32, f32, i32, p, sz, i32, p]
+    lib.paged_attention_decode_shared_workspace_size.restype = sz
+    lib.paged_attention_decode_shared_workspace_size.argtypes = [i32] * 9
+    lib.paged_attention_decode_shared.restype = ctypes.c_int
+    lib.paged_attention_decode_shared.argtypes = [p, p, p, p, i32, p, i32, p, i32, i32, i32, i32,
+                                                  i32, i32, ctypes.c_float, p, p, p, i32, i32,
+                                                  i32, i32, p, sz, i32, p]
     lib.paged_attention_extend.restype = ctypes.c_int
     lib.paged_attention_extend.argtypes = [p, p, p, p, i32, i32, i32, i32, p, p, i32, p, i32,
                                            i32, i32, i32, i32, f32, i32, p]
@@ -157,6 +164,86 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
                                          bs, float(scale), int(partition_size), _ptr(workspace),
                                          wbytes, dt, _stream()))
     return workspace
+
+
+def paged_attention_decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 max_context_len, partition_size, num_groups,
+                                                 max_group_size, max_prefix_blocks):
+    return int(load().paged_attention_decode_shared_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, int(max_context_len), int(partition_size),
+        int(num_groups), int(max_group_size), int(max_prefix_blocks)))
+
+
+def paged_attention_decode_shared(out, q, k_pool, v_pool, block_tables, context_lens,
+                                  max_context_len, scale, groups, partition_size=0,
+                                  workspace=None):
+    """``groups``: ``(group_offsets, group_seqs, group_prefix_blocks, max_group_size,
+    max_prefix_blocks)`` -- three int32 device tensors and two host ints, as
+    :func:`shared_prefix_groups` returns them."""
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    offs, seqs, pblk, max_size, max_pb = groups
+    _dev(out, q, k_pool, v_pool, block_tables, context_lens, offs, seqs, pblk)
+    _int32(block_tables, context_lens, offs, seqs, pblk)
+    S, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (S, hq, d) or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("q/out must be [S][Hq][D] in the pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables [S][max_blocks], context_lens [S]")
+    G = offs.shape[0] - 1
+    if G < 0 or pblk.shape[0] != G:
+        raise ValueError("group_offsets [G+1], group_prefix_blocks [G]")
+    need = paged_attention_decode_shared_workspace_size(S, hq, hkv, d, max_context_len,
+                                                        partition_size, G, max_size, max_pb)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev(workspace)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().paged_attention_decode_shared(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), S, int(max_context_len), hq, hkv, d, bs,
+        float(scale), _ptr(offs), _ptr(seqs), _ptr(pblk), G, int(max_size), int(max_pb),
+        int(partition_size), _ptr(workspace), wbytes, dt, _stream()))
+    return workspace
+
+
+def shared_prefix_groups(tables, lens, block_size=16, min_blocks=1, device=None):
+    """Groups for :func:`paged_attention_decode_shared` from host block tables
+    (numpy int32 ``[S][max_blocks]``) and context lengths: sequences whose
+    first table entry is the same physical block form a group, whose prefix
+    is the longest run of leading entries they all share, cut so that every
+    member keeps its last block for itself.  Groups of one member, or whose
+    prefix is shorter than ``min_blocks``, are left out.  Host-side work on
+    the tables the allocator already holds; returns the ``groups`` tuple with
+    the arrays on ``device``."""
+    import numpy as np
+    tables = np.asarray(tables)
+    lens = np.asarray(lens).astype(np.int64)
+    nb = (lens + block_size - 1) // block_size
+    usable = np.where(lens > 0, (lens - 1) // block_size, 0)   # blocks before the last one
+    first = np.where(nb > 0, tables[:, 0], -1)
+    order = np.argsort(first, kind="stable")
+    offs, seqs, pblk = [0], [], []
+    i = 0
+    while i < len(order):
+        j = i
+        while j < len(order) and first[order[j]] == first[order[i]]:
+            j += 1
+        members = order[i:j]
+        if first[order[i]] >= 0 and len(members) > 1:
+            limit = int(usable[members].min())
+            rows = tables[members, :limit]
+            same = (rows == rows[0]).all(axis=0)
+            k = limit if same.all() else int(np.argmin(same))
+            if k >= min_blocks:
+                seqs += members.tolist()
+                pblk.append(k)
+                offs.append(len(seqs))
+        i = j
+    dev = device if device is not None else "cuda"
+    t = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)
+    return (t(offs), t(seqs), t(pblk), max((offs[g + 1] - offs[g] for g in range(len(pblk))),
+                                           default=0), max(pblk, default=0))
 
 
 def paged_attention_extend(out, q, cu_seqlens_q, seq_lens, k_pool, v_pool, block_tables,

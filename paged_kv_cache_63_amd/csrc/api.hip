@@ -75,6 +75,41 @@ int decode_workgroups() {
   return 2 * cus;
 }
 
+// Key split of the shared-prefix pass: enough splits that the pass's
+// workgroups (groups x KV heads x 256-row tiles x splits) about fill the
+// compute units once, in multiples of the kernel's 4-block key tile.
+struct PrefixSplit {
+  int32_t blocks;   // per split
+  int32_t count;    // splits of the longest prefix
+};
+PrefixSplit prefix_split(int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
+                         int32_t g, int32_t num_kv_heads) {
+  if (num_groups <= 0 || max_group_size <= 0 || max_prefix_blocks <= 0) return {4, 0};
+  const int64_t row_tiles = ((int64_t)max_group_size * g + 255) / 256;
+  const int64_t base = (int64_t)num_groups * num_kv_heads * row_tiles;
+  const int64_t cus = decode_workgroups() / 2;
+  const int64_t want = base >= cus ? 1 : cus / base;
+  int64_t blocks = (max_prefix_blocks + want - 1) / want;
+  blocks = (blocks + 3) / 4 * 4;
+  return {(int32_t)blocks, (int32_t)((max_prefix_blocks + blocks - 1) / blocks)};
+}
+
+// Byte offsets of the shared-prefix decode's workspace regions.
+struct SharedLayout {
+  size_t seq_prefix, pre_o, pre_m, pre_l, total;
+};
+SharedLayout shared_layout(int64_t S, int64_t hq, int64_t hkv, int64_t D, int64_t P, int64_t NS) {
+  SharedLayout l{};
+  const size_t dec = (size_t)S * hq * P * (D + 2) * 4 + (size_t)S * hkv * 4;
+  l.seq_prefix = dec;
+  const size_t after = dec + (size_t)S * 2 * 4;
+  l.pre_o = (after + 255) / 256 * 256;
+  l.pre_m = l.pre_o + (size_t)S * hq * NS * D * 4;
+  l.pre_l = l.pre_m + (size_t)S * hq * NS * 4;
+  l.total = l.pre_l + (size_t)S * hq * NS * 4;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +236,138 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   a.scale = scale;
   rc = pkv::launch_decode(a, dtype, (hipStream_t)stream);
   return rc ? fail(rc, "decode launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();
+}
+
+size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_context_len, int32_t partition_size,
+                                                    int32_t num_groups, int32_t max_group_size,
+                                                    int32_t max_prefix_blocks) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0 || num_groups < 0 || max_group_size < 0 || max_prefix_blocks < 0 ||
+      num_q_heads % num_kv_heads)
+    return 0;
+  const int32_t ptok = choose_piece(partition_size);
+  if (ptok <= 0) return 0;
+  const int64_t P = max_pieces(max_context_len, ptok);
+  const PrefixSplit sp = prefix_split(num_groups, max_group_size, max_prefix_blocks,
+                                      num_q_heads / num_kv_heads, num_kv_heads);
+  return shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, P, sp.count).total;
+}
+
+int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
+                                  const void* v_pool, int32_t num_blocks,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  float scale, const int32_t* group_offsets,
+                                  const int32_t* group_seqs, const int32_t* group_prefix_blocks,
+                                  int32_t num_groups, int32_t max_group_size,
+                                  int32_t max_prefix_blocks, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  void* stream) {
+  int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
+  if (rc) return rc;
+  if (num_groups < 0 || max_group_size < 0 || max_prefix_blocks < 0)
+    return fail(PKV_ERR_INVALID, "negative group argument");
+  if (dtype != PKV_DTYPE_BF16 || num_groups == 0 || max_group_size == 0 || max_prefix_blocks == 0)
+    // nothing shared (or fp32, whose path has no prefix pass): the plain decode
+    return paged_attention_decode(out, q, k_pool, v_pool, num_blocks, block_tables,
+                                  max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                                  num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                                  partition_size, workspace, workspace_bytes, dtype, stream);
+  rc = check_heads(num_q_heads, num_kv_heads);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID, "bad num_seqs/num_blocks/max_blocks_per_seq/max_context_len");
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !group_offsets ||
+      !group_seqs || !group_prefix_blocks)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (max_group_size > num_seqs || max_prefix_blocks > max_blocks_per_seq)
+    return fail(PKV_ERR_INVALID, "max_group_size %d > num_seqs or max_prefix_blocks %d > "
+                "max_blocks_per_seq", max_group_size, max_prefix_blocks);
+  if ((int64_t)num_seqs * num_q_heads > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "too many sequences");
+  const int32_t ptok = choose_piece(partition_size);
+  if (ptok < 0 || ptok % block_size)
+    return fail(PKV_ERR_INVALID, "partition_size %d must be a multiple of %d", partition_size,
+                block_size);
+  const int64_t P = max_pieces(max_context_len, ptok);
+  const int32_t g = num_q_heads / num_kv_heads;
+  const PrefixSplit sp = prefix_split(num_groups, max_group_size, max_prefix_blocks, g, num_kv_heads);
+  if (P > kMaxPieces || (2 * g * (P + sp.count) + 16) * 4 > 160 * 1024 - 256)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "max_context_len %d over partition_size %d gives %lld pieces per context; use a "
+                "larger partition_size", max_context_len, ptok, (long long)P);
+  const SharedLayout lay = shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, P, sp.count);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                workspace_bytes);
+
+  uint8_t* ws = (uint8_t*)workspace;
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  {
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * P;
+    a.part_o = (float*)ws;
+    a.part_m = a.part_o + rows * head_dim;
+    a.part_l = a.part_m + rows;
+    a.counters = (int32_t*)(a.part_l + rows);
+  }
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.partition_blocks = ptok / block_size;
+  a.max_partitions = (int32_t)P;
+  a.num_workgroups = decode_workgroups();
+  a.scale = scale;
+  a.seq_prefix = (int32_t*)(ws + lay.seq_prefix);
+  a.pre_o = (float*)(ws + lay.pre_o);
+  a.pre_m = (float*)(ws + lay.pre_m);
+  a.pre_l = (float*)(ws + lay.pre_l);
+  a.num_splits = sp.count;
+
+  pkv::PrefixArgs p{};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.group_offsets = group_offsets;
+  p.group_seqs = group_seqs;
+  p.group_prefix_blocks = group_prefix_blocks;
+  p.pre_o = (float*)a.pre_o;
+  p.pre_m = (float*)a.pre_m;
+  p.pre_l = (float*)a.pre_l;
+  p.seq_prefix = (int32_t*)a.seq_prefix;
+  p.num_groups = num_groups;
+  p.max_group_size = max_group_size;
+  p.num_seqs = num_seqs;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.split_blocks = sp.blocks;
+  p.num_splits = sp.count;
+  p.scale = scale;
+
+  hipStream_t st = (hipStream_t)stream;
+  // counters and seq_prefix are adjacent: one clear for both
+  rc = pkv::clear_ints(a.counters, (int64_t)num_seqs * (num_kv_heads + 2), st);
+  if (!rc) rc = pkv::launch_prefix(p, st);
+  if (!rc) rc = pkv::launch_decode(a, dtype, st);
+  return rc ? fail(rc, "shared-prefix decode launch failed: %s", hipGetErrorString(hipGetLastError()))
+            : ok();
 }
 
 int paged_attention_extend(void* out, const void* q, const int32_t* cu_seqlens_q,

@@ -75,9 +75,20 @@ struct DecodeArgs {
   int32_t max_partitions;    // P: pieces per (sequence, query head) the workspace holds
   int32_t num_workgroups;    // bf16 grid
   float scale;
+  // Shared-prefix decode only (null / 0 otherwise): per sequence, the first
+  // block its own pass starts at and how many prefix partials (pre_*, one
+  // per key split of the prefix pass) its result folds in.
+  const int32_t* seq_prefix; // [S][2]: start block, number of prefix partials
+  const float* pre_o;        // [S][Hq][num_splits][D]
+  const float* pre_m;        // [S][Hq][num_splits]
+  const float* pre_l;        // [S][Hq][num_splits]
+  int32_t num_splits;
 };
 
 int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st);
+
+// Zero n int32 words with a kernel (graph-capturable, unlike a memset).
+int clear_ints(int32_t* p, int64_t n, hipStream_t st);
 
 struct ExtendArgs {
   void* out;
@@ -100,5 +111,38 @@ struct ExtendArgs {
 };
 
 int launch_extend(const ExtendArgs& a, int32_t dtype, hipStream_t st);
+
+// Prefix pass of the shared-prefix decode: for every group of sequences
+// whose tables begin with the same prefix_blocks physical blocks, attention
+// of all the members' query heads over those blocks, split along the keys
+// into pieces of split_blocks blocks; writes each piece's (normalised o, m,
+// l) per (sequence, query head) and each member's seq_prefix entry.
+struct PrefixArgs {
+  const void* q;             // [S][Hq][D]
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* group_offsets;       // [G+1]
+  const int32_t* group_seqs;          // members, group-major
+  const int32_t* group_prefix_blocks; // [G]
+  float* pre_o;
+  float* pre_m;
+  float* pre_l;
+  int32_t* seq_prefix;       // [S][2]
+  int32_t num_groups;
+  int32_t max_group_size;
+  int32_t num_seqs;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t split_blocks;      // a multiple of 4
+  int32_t num_splits;
+  float scale;
+};
+
+int launch_prefix(const PrefixArgs& a, hipStream_t st);
 
 }  // namespace pkv

@@ -113,7 +113,9 @@ __device__ __forceinline__ int64_t wg_scan(int64_t v, int64_t* red, int64_t* tot
 
 // At most 128 VGPRs (four waves per SIMD): two workgroups per compute unit
 // stay resident, the number the grid is sized for.
-template <int D, int NW>
+// SHARED: the shared-prefix variant (seq_prefix and the prefix partials are
+// read); a template flag so that the plain decode's code is unaffected.
+template <int D, int NW, bool SHARED>
 __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int64_t red[NW];
@@ -135,7 +137,21 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   const int W = gridDim.x;
   const int w = blockIdx.x;
   uint16_t* out = (uint16_t*)a.out;
-  auto nblocks = [&](int s) { return (usable_len(a, s) + kBs - 1) / kBs; };
+  // Shared-prefix decode: sequence s's own pass covers its blocks from
+  // start_block(s) on; the prefix pass has left n_prefix(s) partials for
+  // the blocks before it, which its result folds in.
+  auto start_block = [&](int s, int nb) {
+    if constexpr (SHARED) return min(a.seq_prefix[2 * s], max(nb - 1, 0));
+    else return 0;
+  };
+  auto n_prefix = [&](int s) {
+    if constexpr (SHARED) return a.seq_prefix[2 * s + 1];
+    else return 0;
+  };
+  auto nblocks = [&](int s) {
+    const int nb = (usable_len(a, s) + kBs - 1) / kBs;
+    return nb - start_block(s, nb);
+  };
 
   // Plan, part 1: total work; empty contexts get a zero row (workgroup
   // s mod W writes it).
@@ -183,6 +199,8 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   float* sm_m = smem + NW * g * D;     // [NW][16]
   float* sm_l = sm_m + NW * 16;        // [NW][16]
 
+  const int NS = a.num_splits;
+  int nsp = 0;   // prefix partials of the sequence a piece belongs to
   // One piece: blocks [bb, be) of unit (s, h); piece k of np.
   auto piece = [&](int s, int h, int L, int bb, int be, int k, int np) {
     // Q^T operand: lane (head column col, group grp) holds 8 channels per product.
@@ -289,8 +307,21 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
         acc += sm_o[(v * g + c) * D + dd] * f;
       }
       const int64_t row = (int64_t)s * hq + h * g + c;
-      if (np == 1) {
+      if (np == 1 && (!SHARED || nsp == 0)) {
         out[row * D + dd] = f32_to_bf16(acc / lsum);
+      } else if (SHARED && np == 1) {
+        // fold in the prefix pass's partials (log-sum-exp rule, natural log)
+        const float ms = M * kLn2;
+        float Mx = ms;
+        for (int j = 0; j < nsp; ++j) Mx = fmaxf(Mx, a.pre_m[row * NS + j]);
+        float den = lsum * expf(ms - Mx);
+        float num = acc * expf(ms - Mx);   // (acc / lsum) * lsum * e^(ms - Mx)
+        for (int j = 0; j < nsp; ++j) {
+          const float wj = a.pre_l[row * NS + j] * expf(a.pre_m[row * NS + j] - Mx);
+          num = fmaf(wj, a.pre_o[(row * NS + j) * D + dd], num);
+          den += wj;
+        }
+        out[row * D + dd] = f32_to_bf16(num / den);
       } else {
         put(&a.part_o[(row * P + k) * D + dd], acc / lsum);
         if (dd == 0) {
@@ -305,14 +336,22 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   // last): the pieces' weights l_j e^(m_j - M) go through LDS (one load per
   // (head, piece) across the workgroup), then every (head, channel) thread
   // sums its o_j with eight loads in flight.
-  auto merge = [&](int s, int h, int np) {
+  // Prefix partials of a shared-prefix decode count as pieces np..np+nsp-1
+  // (written by an earlier kernel: plain loads).
+  auto merge = [&](int s, int h, int np_own, int nsp) {
+    const int np = np_own + nsp;
     float* sw = smem;   // [g][np] m, [g][np] weights, [g] inverse sums
     for (int idx = tid; idx < g * np; idx += NT) {
       const int c = idx / np;
       const int j = idx - c * np;
       const int64_t row = (int64_t)s * hq + h * g + c;
-      sw[idx] = get(&a.part_m[row * P + j]);
-      sw[g * np + idx] = get(&a.part_l[row * P + j]);
+      if (!SHARED || j < np_own) {
+        sw[idx] = get(&a.part_m[row * P + j]);
+        sw[g * np + idx] = get(&a.part_l[row * P + j]);
+      } else {
+        sw[idx] = a.pre_m[row * NS + j - np_own];
+        sw[g * np + idx] = a.pre_l[row * NS + j - np_own];
+      }
     }
     __syncthreads();
     if (tid < g) {
@@ -333,14 +372,16 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
       const int64_t row = (int64_t)s * hq + h * g + c;
       const float* wts = sw + g * np + c * np;
       float acc = 0.f;
-      for (int j0 = 0; j0 < np; j0 += 8) {
+      for (int j0 = 0; j0 < np_own; j0 += 8) {
         float ov[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ov[u] = get(&a.part_o[(row * P + min(j0 + u, np - 1)) * D + dd]);
+        for (int u = 0; u < 8; ++u) ov[u] = get(&a.part_o[(row * P + min(j0 + u, np_own - 1)) * D + dd]);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (j0 + u < np) acc = fmaf(wts[j0 + u], ov[u], acc);
+          if (j0 + u < np_own) acc = fmaf(wts[j0 + u], ov[u], acc);
       }
+      if constexpr (SHARED)
+        for (int j = 0; j < nsp; ++j) acc = fmaf(wts[np_own + j], a.pre_o[(row * NS + j) * D + dd], acc);
       out[row * D + dd] = f32_to_bf16(acc * sw[2 * g * np + c]);
     }
     __syncthreads();   // the LDS is reused by the next merge
@@ -353,14 +394,17 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   int pend_s[2] = {0, 0}, pend_h[2] = {0, 0}, pend_np[2] = {0, 0};
   while (G < hi && s < S) {
     const int L = usable_len(a, s);
-    const int nb = (L + kBs - 1) / kBs;
+    const int nb_all = (L + kBs - 1) / kBs;
+    const int st = start_block(s, nb_all);
+    const int nb = nb_all - st;
+    nsp = n_prefix(s);
     for (int h = 0; h < hkv; ++h) {
       const int64_t Gh = G + (int64_t)h * nb;
       const int64_t a0 = max(lo, Gh), a1 = min(hi, Gh + nb);
       if (a0 < a1) {
         const int k = (int)(w - Gh / C);
         const int np = (int)((Gh + nb - 1) / C - Gh / C + 1);
-        piece(s, h, L, (int)(a0 - Gh), (int)(a1 - Gh), k, np);
+        piece(s, h, L, st + (int)(a0 - Gh), st + (int)(a1 - Gh), k, np);
         if (np > 1 && n_pend < 2) {
           pend_s[n_pend] = s;
           pend_h[n_pend] = h;
@@ -390,7 +434,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   }
   __syncthreads();
   for (int i = 0; i < n_pend; ++i)
-    if (sh_lastv[i]) merge(pend_s[i], pend_h[i], pend_np[i]);
+    if (sh_lastv[i]) merge(pend_s[i], pend_h[i], pend_np[i], n_prefix(pend_s[i]));
 }
 
 // ---------------------------------------------------------------- fp32 pass 1
@@ -568,20 +612,23 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     constexpr int NW = 8;
     // wave-merge area [NW][g][D] + [NW][16] m + [NW][16] l, also used for
     // the piece weights of a merge ([2][g][P] + [g])
-    const size_t words = (size_t)max(NW * g * D + 2 * NW * 16, 2 * g * a.max_partitions + g);
+    const size_t words =
+        (size_t)max(NW * g * D + 2 * NW * 16, 2 * g * (a.max_partitions + a.num_splits) + g);
     const size_t lds = words * sizeof(float);
     if (lds > kDecodeLdsMax) return -2;
-    auto kern = decode_bf16_kernel<D, NW>;
-    static bool attr_set = false;   // dynamic LDS above 64 KB needs the limit raised once
-    if (!attr_set) {
+    auto kern = a.seq_prefix ? decode_bf16_kernel<D, NW, true> : decode_bf16_kernel<D, NW, false>;
+    static bool attr_set[2] = {false, false};   // dynamic LDS above 64 KB needs the limit raised once
+    if (!attr_set[a.seq_prefix != nullptr]) {
       if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kDecodeLdsMax) != hipSuccess)
         return -4;
-      attr_set = true;
+      attr_set[a.seq_prefix != nullptr] = true;
     }
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t cgrid = (units + 255) / 256;
-    clear_counters_kernel<<<(int)(cgrid < 1024 ? (cgrid > 0 ? cgrid : 1) : 1024), 256, 0, st>>>(a.counters, units);
+    if (!a.seq_prefix)   // the shared-prefix entry clears them with its own table
+      clear_counters_kernel<<<(int)(cgrid < 1024 ? (cgrid > 0 ? cgrid : 1) : 1024), 256, 0, st>>>(
+          a.counters, units);
     kern<<<a.num_workgroups, NW * kWave, lds, st>>>(a);
     return status_of(hipGetLastError());
   }
@@ -599,6 +646,13 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
 }
 
 }  // namespace
+
+int clear_ints(int32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return 0;
+  const int64_t cgrid = (n + 255) / 256;
+  clear_counters_kernel<<<(int)(cgrid < 1024 ? cgrid : 1024), 256, 0, st>>>(p, n);
+  return status_of(hipGetLastError());
+}
 
 int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
   if (a.num_seqs == 0) return 0;

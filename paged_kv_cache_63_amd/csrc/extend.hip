@@ -56,6 +56,7 @@ namespace pkv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBs = 16;
 constexpr int kXcds = 8;
 
@@ -122,8 +123,18 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, u
 // block and 8..15 the second, in exactly the slot order P^T needs when V^T
 // slot (hb, e) holds key 8*hb + 4G + e, i.e. two 8-byte reads of a
 // channel's 32-byte row.  No shuffles between the two products.
-template <int D>
-__global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, int tiles_per_unit,
+//
+// PREFIX: the prefix pass of the shared-prefix decode.  A unit is (group,
+// KV head, key split); its rows are (member, query head of the group), the
+// member's single query token taking the place of a new token; its keys are
+// the split's range of the prefix blocks (read through the first member's
+// table), starting at key tile kt0.  A member sees the prefix keys below
+// its own start block (keys past it are masked like causal ones), and a row
+// may see no key of a split at all, so the exponent reference of such a row
+// is taken as 0 instead of -inf.  Output: the normalised partial (o, m in
+// natural-log units, l) per (member, query head, split).
+template <int D, bool PREFIX, typename Args>
+__global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tiles_per_unit,
                                                                 int units) {
   constexpr int NW = 8;
   constexpr int HALF = NW / 2;            // waves per group: one per SIMD
@@ -157,16 +168,50 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   const int unit = bid % kXcds + kXcds * (slot / tiles_per_unit);
   if (unit >= units) return;
   const int tile = tiles_per_unit - 1 - slot % tiles_per_unit;
-  const int r = unit / hkv;
-  const int h = unit - r * hkv;
-  const int q0 = a.cu_seqlens_q[r];
-  const int n = a.cu_seqlens_q[r + 1] - q0;
-  int L = a.seq_lens[r];
   const int row0 = tile * ROWS;
-  if (n <= 0 || row0 >= n * g || q0 < 0 || q0 + n > a.total_q) return;
-  if (L > a.max_blocks_per_seq * kBs) L = a.max_blocks_per_seq * kBs;
-  const int P = L - n;
-  if (P < 0) return;
+  int r, h, n, L, P = 0, q0 = 0;
+  int kt0 = 0;                        // first key tile of the unit
+  int goff = 0, split = 0, pblk = 0;  // prefix pass: group's first member, split, prefix blocks
+  if constexpr (!PREFIX) {
+    r = unit / hkv;
+    h = unit - r * hkv;
+    q0 = a.cu_seqlens_q[r];
+    n = a.cu_seqlens_q[r + 1] - q0;
+    L = a.seq_lens[r];
+    if (n <= 0 || row0 >= n * g || q0 < 0 || q0 + n > a.total_q) return;
+    if (L > a.max_blocks_per_seq * kBs) L = a.max_blocks_per_seq * kBs;
+    P = L - n;
+    if (P < 0) return;
+  } else {
+    const int per_group = hkv * a.num_splits;
+    const int grp = unit / per_group;
+    const int rem = unit - grp * per_group;
+    h = rem / a.num_splits;
+    split = rem - h * a.num_splits;
+    goff = a.group_offsets[grp];
+    n = a.group_offsets[grp + 1] - goff;   // members
+    // (at most what the splits cover: the host sized them for the longest prefix)
+    pblk = min(min(max(a.group_prefix_blocks[grp], 0), a.max_blocks_per_seq),
+               a.num_splits * a.split_blocks);
+    if (goff < 0 || n <= 0 || n > a.max_group_size || row0 >= n * g) return;
+    if (row0 == 0 && h == 0 && split == 0) {
+      // each member's own pass starts at its first block past the prefix
+      // that still leaves it one token (the decoded one): its last block
+      for (int m = threadIdx.x; m < n; m += NW * kWave) {
+        const int s = a.group_seqs[goff + m];
+        if (s < 0 || s >= a.num_seqs) continue;
+        const int Ls = a.context_lens[s];
+        a.seq_prefix[2 * s] = Ls >= 1 ? min(pblk, (Ls - 1) / kBs) : 0;
+        a.seq_prefix[2 * s + 1] = Ls >= 1 ? (pblk + a.split_blocks - 1) / a.split_blocks : 0;
+      }
+    }
+    const int klo = split * a.split_blocks * kBs;
+    L = min(pblk * kBs, klo + a.split_blocks * kBs);   // keys at or past L are masked
+    if (klo >= L) return;
+    kt0 = klo / KT;
+    r = a.group_seqs[goff];     // the first member's table supplies the prefix blocks
+    if (r < 0 || r >= a.num_seqs) return;
+  }
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -178,21 +223,22 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
 
   // Rows of this workgroup and their last visible key.
   const int last_row = min(row0 + ROWS, n * g) - 1;
-  const int kend = P + last_row / g + 1;                   // keys 0..kend-1 are needed
-  const int ntiles = (kend + KT - 1) / KT;
   const int wrow0 = row0 + wave * RPW;
   const bool has_rows = wrow0 <= last_row;
-  const int wq_min = P + min(wrow0, last_row) / g;         // smallest query position of the wave
-  const int wq_max = has_rows ? P + min(wrow0 + RPW - 1, last_row) / g : -1;
+  int ntiles, wq_min, wq_max;
 
   // Q^T operand: lane (row c32, group G) holds channels ks*16 + G*8 .. +7
   // (loaded after the first tile copies have been issued).
   const uint16_t* qp = (const uint16_t*)a.q;
   bf16x8 qf[KS];
-  int qpos;
+  int qpos;                 // the row's last visible key
   const uint16_t* qrow;
   bool qlive;
-  {
+  if constexpr (!PREFIX) {
+    const int kend = P + last_row / g + 1;                 // keys 0..kend-1 are needed
+    ntiles = (kend + KT - 1) / KT;
+    wq_min = P + min(wrow0, last_row) / g;                 // smallest query position of the wave
+    wq_max = has_rows ? P + min(wrow0 + RPW - 1, last_row) / g : -1;
     const int rr = wrow0 + c32;
     const bool live = rr <= last_row;
     const int t = live ? rr / g : 0;
@@ -200,6 +246,25 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
     qpos = P + (live ? t : last_row / g);
     qrow = qp + ((int64_t)(q0 + t) * hq + h * g + j) * D + G * 8;
     qlive = live;
+  } else {
+    ntiles = (L - kt0 * KT + KT - 1) / KT;
+    const int rr = wrow0 + c32;
+    int s = rr <= last_row ? a.group_seqs[goff + rr / g] : -1;
+    const bool live = s >= 0 && s < a.num_seqs;
+    const int j = rr - (rr / g) * g;
+    const int Ls = live ? a.context_lens[s] : 0;
+    const int start = Ls >= 1 ? min(pblk, (Ls - 1) / kBs) : 0;
+    qpos = live ? min(start * kBs, L) - 1 : -1;
+    qrow = qp + ((int64_t)(live ? s : 0) * hq + h * g + (live ? j : 0)) * D + G * 8;
+    qlive = live;
+    int lo = live ? qpos : (1 << 30), hi = live ? qpos : -1;
+#pragma unroll
+    for (int k = 1; k < 32; k <<= 1) {
+      lo = min(lo, __shfl_xor(lo, k, kWave));
+      hi = max(hi, __shfl_xor(hi, k, kWave));
+    }
+    wq_min = __builtin_amdgcn_readfirstlane(lo);
+    wq_max = __builtin_amdgcn_readfirstlane(hi);
   }
 
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
@@ -243,13 +308,13 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   const int64_t blk_stride = (int64_t)hkv * BLKB;   // bytes between physical blocks
   auto fetch_entries = [&](int t, int (&e)[PER_T]) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) e[i] = entry_raw(t * NBT + src_blk[i]);
+    for (int i = 0; i < PER_T; ++i) e[i] = entry_raw((t + kt0) * NBT + src_blk[i]);
   };
   auto issue = [&](int t, const int (&e)[PER_T]) {
     const int st = t % NST;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int phys = entry_ok(t * NBT + src_blk[i], e[i]);
+      const int phys = entry_ok((t + kt0) * NBT + src_blk[i], e[i]);
       const uint8_t* base = (src_v[i] ? vpool : kpool) + (int64_t)phys * blk_stride;
       const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)(
           &kv_s[st][(i * NW + wave) * kWave * 16]);
@@ -400,13 +465,17 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
     const bool grow = m_new > m_ref + kLazy;
     if (__any(grow)) {   // rare after the first tile
       const float target = grow ? m_new : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - target);
+      float alpha = __builtin_amdgcn_exp2f(m_ref - target);
+      // a row that has seen no key keeps m_ref = -inf: exp2(-inf - -inf) is
+      // not 1, so rows that do not grow take alpha = 1 explicitly
+      if constexpr (PREFIX) alpha = grow ? alpha : 1.f;
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m_ref = target;
     }
-    const float nm = -m_ref;
+    float nm = -m_ref;
+    if constexpr (PREFIX) nm = m_ref == -INFINITY ? 0.f : nm;   // a row with no key yet
 #pragma unroll
     for (int b = 0; b < NBT; ++b) {
       float p[8];
@@ -487,8 +556,8 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   // This wave computes on tiles 0..nt-1 (later tiles are in the future of
   // all its rows), with the causal mask from tile td on; a tile past the end
   // of the sequence can only be the last one, whose PV has no QK after it.
-  const int nt = has_rows ? min(ntiles, wq_max / KT + 1) : 0;
-  const int td = (wq_min + 1) / KT;
+  const int nt = has_rows && wq_max >= kt0 * KT ? min(ntiles, (wq_max - kt0 * KT) / KT + 1) : 0;
+  const int td = wq_min + 1 >= kt0 * KT ? (wq_min + 1 - kt0 * KT) / KT : 0;
   {
     int e0[PER_T], e1[PER_T], e2[PER_T];
     fetch_entries(0, e0);
@@ -517,7 +586,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   for (; t < t_plain; ++t) {          // no mask, PV and QK
     end_phase(2 * t + lag);
     copy_and_lookup(t);
-    softmax(t * KT, std::false_type{});
+    softmax((t + kt0) * KT, std::false_type{});
     pre_read(t % NST);
     end_phase(2 * t + 1 + lag);
     pv_qk(t % NST, (t + 1) % NST);
@@ -525,7 +594,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   for (; t < nt - 1; ++t) {           // masked, PV and QK
     end_phase(2 * t + lag);
     copy_and_lookup(t);
-    softmax(t * KT, std::true_type{});
+    softmax((t + kt0) * KT, std::true_type{});
     pre_read(t % NST);
     end_phase(2 * t + 1 + lag);
     pv_qk(t % NST, (t + 1) % NST);
@@ -533,10 +602,10 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   if (t < nt) {                        // last tile of this wave: PV only
     end_phase(2 * t + lag);
     copy_and_lookup(t);
-    if (t < td) softmax(t * KT, std::false_type{});
-    else softmax(t * KT, std::true_type{});
+    if (t < td) softmax((t + kt0) * KT, std::false_type{});
+    else softmax((t + kt0) * KT, std::true_type{});
     end_phase(2 * t + 1 + lag);
-    pv(t % NST, t * KT);
+    pv(t % NST, (t + kt0) * KT);
     ++t;
   }
   for (; t < ntiles; ++t) {           // copies and barriers only
@@ -551,6 +620,25 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
   const float l = lsum[0];
   const int rr = wrow0 + c32;
   if (rr > last_row) return;
+  if constexpr (PREFIX) {
+    if (!qlive) return;
+    const int s = a.group_seqs[goff + rr / g];
+    const int64_t prow = ((int64_t)s * hq + h * g + (rr - (rr / g) * g)) * a.num_splits + split;
+    const float inv = l > 0.f ? 1.f / l : 0.f;   // a row that saw no key: o = 0, weight 0
+    float* orow = a.pre_o + prow * D + G * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<f32x4*>(orow + dt * 32 + b * 8) =
+            f32x4{o[dt][4 * b] * inv, o[dt][4 * b + 1] * inv, o[dt][4 * b + 2] * inv,
+                  o[dt][4 * b + 3] * inv};
+    if (G == 0) {
+      a.pre_m[prow] = l > 0.f ? m_ref * kLn2 : -INFINITY;   // natural-log units
+      a.pre_l[prow] = l;
+    }
+    return;
+  } else {
   const int tok = rr / g;
   const int jh = rr - tok * g;
   const float inv = 1.f / l;
@@ -565,6 +653,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(ExtendArgs a, in
                           ((uint32_t)f32_to_bf16(o[dt][4 * b + 3] * inv) << 16);
       *reinterpret_cast<u32x2*>(orow + dt * 32 + b * 8) = u32x2{w0, w1};
     }
+  }
 }
 
 // fp32: one wave per (new token, KV head); the g query heads of the group
@@ -666,7 +755,7 @@ int launch_e(const ExtendArgs& a, int32_t dtype, hipStream_t st) {
     const int64_t grid = (int64_t)kXcds * unit_groups * tiles;
     if (grid == 0) return 0;
     if (grid > 0x7fffffff) return -1;
-    extend_bf16_kernel<D><<<(unsigned)grid, NW * kWave, 0, st>>>(a, tiles, units);
+    extend_bf16_kernel<D, false><<<(unsigned)grid, NW * kWave, 0, st>>>(a, tiles, units);
   } else {
     if (a.max_q_len == 0) return 0;
     extend_f32_kernel<D><<<dim3(a.max_q_len, a.num_kv_heads, a.num_reqs), kWave, 0, st>>>(a);
@@ -674,7 +763,27 @@ int launch_e(const ExtendArgs& a, int32_t dtype, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+template <int D>
+int launch_p(const PrefixArgs& a, hipStream_t st) {
+  constexpr int ROWS = 8 * 32;
+  const int g = a.num_q_heads / a.num_kv_heads;
+  const int tiles = (a.max_group_size * g + ROWS - 1) / ROWS;
+  const int64_t units = (int64_t)a.num_groups * a.num_kv_heads * a.num_splits;
+  const int64_t unit_groups = (units + kXcds - 1) / kXcds;
+  const int64_t grid = (int64_t)kXcds * unit_groups * tiles;
+  if (grid == 0) return 0;
+  if (grid > 0x7fffffff || units > 0x7fffffff) return -1;
+  extend_bf16_kernel<D, true><<<(unsigned)grid, 8 * kWave, 0, st>>>(a, tiles, (int)units);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 }  // namespace
+
+int launch_prefix(const PrefixArgs& a, hipStream_t st) {
+  if (a.num_groups == 0 || a.max_group_size == 0) return 0;
+  if (a.head_dim == 128) return launch_p<128>(a, st);
+  return launch_p<64>(a, st);
+}
 
 int launch_extend(const ExtendArgs& a, int32_t dtype, hipStream_t st) {
   if (a.num_reqs == 0 || a.total_q == 0) return 0;

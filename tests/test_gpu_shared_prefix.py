@@ -44,8 +44,14 @@ def lib_side(c):
     q = to_dev(c.q, c.dtype)
     out = torch.empty_like(q)
     _lib.paged_attention_decode(out, q, k, v, tables, lens, int(alloc.lens[order].max()), c.scale)
+    # the same batch through the shared-prefix decode (groups found from the tables)
+    groups = _lib.shared_prefix_groups(alloc.tables[order], alloc.lens[order])
+    out_shared = torch.full_like(q, float("nan"))
+    if c.dtype == "bf16":
+        _lib.paged_attention_decode_shared(out_shared, q, k, v, tables, lens,
+                                           int(alloc.lens[order].max()), c.scale, groups)
     return dict(alloc=alloc, order=order, k=k, v=v, out=out, pairs=pairs, slots=step_slots,
-                tables=alloc.tables[order])
+                tables=alloc.tables[order], out_shared=out_shared, groups=groups)
 
 
 def oracle_side(c):
@@ -99,6 +105,12 @@ def _check(c, sample=None):
     rows = range(len(ref["lens"])) if sample is None else sample
     err = max(np.abs(got[s] - want[s]).max() for s in rows)
     assert err <= (1e-5 if c.dtype == "fp32" else 2e-2), err
+    if c.dtype == "bf16":
+        got = f64_of(lib["out_shared"])
+        assert np.isfinite(got).all()
+        err = max(np.abs(got[s] - want[s]).max() for s in rows)
+        print("shared-prefix decode max err", err)
+        assert err <= 2e-2, err
     return lib, ref
 
 
@@ -121,3 +133,5 @@ def test_shared_prefix_full_size(gpu):
                     set(range(256, 268)))
     lib, ref = _check(c, sample=sample)
     assert len(ref["pairs"]) == 12
+    # one group: all 268 sequences behind the prompt's 256 blocks
+    assert lib["groups"][0].cpu().tolist() == [0, 268] and lib["groups"][4] == 256

@@ -98,3 +98,50 @@ def test_empty_calls_are_no_ops(lib):
     assert lib.paged_kv_append(null, null, null, 0, null, null, 10, 8, 128, 16, 1, None) == 0
     assert lib.copy_blocks(null, null, 10, null, 0, 8, 128, 16, 1, None) == 0
     assert lib.paged_kv_last_error() == b""
+
+
+def test_shared_workspace_layout(lib):
+    """The plain decode's regions, then seq_prefix [S][2] int32, then at the
+    next 256-byte boundary the prefix partials o [S][Hq][NS][D], m, l.  NS:
+    the prefix pass aims at one workgroup per compute unit (256 on MI355X,
+    also the value used where no device is visible): 268 members x 4 heads =
+    5 row tiles of 256, x 8 KV heads = 40 workgroups per split, so 6 splits
+    of ceil(256 / 6) = 43 -> 44 blocks (a multiple of the 4-block tile)."""
+    ws = lib.paged_attention_decode_shared_workspace_size
+    S, hq, hkv, D = 268, 32, 8, 128
+    P = 5200 // 512 + 1 + 1
+    dec = S * hq * P * (D + 2) * 4 + S * hkv * 4
+    pre_o = -(-(dec + S * 2 * 4) // 256) * 256
+    NS = 6
+    assert ws(S, hq, hkv, D, 5200, 512, 1, 268, 256) == pre_o + S * hq * NS * (D + 2) * 4
+    # many groups: one split each
+    assert ws(S, hq, hkv, D, 5200, 512, 64, 8, 256) == pre_o + S * hq * 1 * (D + 2) * 4
+    # no groups: no prefix partials
+    assert ws(S, hq, hkv, D, 5200, 512, 0, 0, 0) == pre_o
+    assert ws(0, hq, hkv, D, 5200, 512, 1, 1, 1) == 0
+
+
+def test_shared_bad_arguments_rejected(lib):
+    one = ctypes.c_void_p(8)
+    null = ctypes.c_void_p(0)
+    f = ctypes.c_float(0.1)
+    # a group bigger than the batch
+    rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 4, one, 2, 64, 32, 8, 128,
+                                           16, f, one, one, one, 1, 3, 2, 0, null, 0, 1, None)
+    assert rc == -1 and b"max_group_size" in lib.paged_kv_last_error()
+    # a prefix longer than the table
+    rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 4, one, 2, 64, 32, 8, 128,
+                                           16, f, one, one, one, 1, 2, 5, 0, null, 0, 1, None)
+    assert rc == -1
+    # null group arrays
+    rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 4, one, 2, 64, 32, 8, 128,
+                                           16, f, null, one, one, 1, 2, 2, 0, null, 0, 1, None)
+    assert rc == -1
+    # missing workspace
+    rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 4, one, 2, 64, 32, 8, 128,
+                                           16, f, one, one, one, 1, 2, 2, 0, null, 0, 1, None)
+    assert rc == -3
+    # negative counts
+    rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 4, one, 2, 64, 32, 8, 128,
+                                           16, f, one, one, one, -1, 2, 2, 0, null, 0, 1, None)
+    assert rc == -1
