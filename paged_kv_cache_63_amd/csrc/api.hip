@@ -88,7 +88,8 @@ PrefixSplit prefix_split(int32_t num_groups, int32_t max_group_size, int32_t max
   const int64_t row_tiles = ((int64_t)max_group_size * g + 255) / 256;
   const int64_t base = (int64_t)num_groups * num_kv_heads * row_tiles;
   const int64_t cus = decode_workgroups() / 2;
-  const int64_t want = base >= cus ? 1 : cus / base;
+  // at most 8 splits: each member's merge folds in every split's partial
+  const int64_t want = base >= cus ? 1 : (cus / base < 8 ? cus / base : 8);
   int64_t blocks = (max_prefix_blocks + want - 1) / want;
   blocks = (blocks + 3) / 4 * 4;
   return {(int32_t)blocks, (int32_t)((max_prefix_blocks + blocks - 1) / blocks)};

@@ -5,6 +5,9 @@
 // ranges to a fixed grid of workgroups; a (sequence, KV head) unit that
 // straddles ranges is computed in pieces and merged by its last piece
 // (log-sum-exp rule), so the merge needs no second launch.
+// Shared-prefix variant (bf16): each sequence's pass starts after the blocks
+// a prefix pass has already covered, every piece leaves a partial, and a
+// small kernel then merges each unit's pieces with the prefix partials.
 // fp32: a plain vector-ALU pass over fixed partitions (one wave per
 // workgroup, exact expf), then a merge pass for contexts with more than one
 // partition: out = sum_p o_p l_p e^(m_p-M) / sum_p l_p e^(m_p-M).
@@ -138,14 +141,9 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   const int w = blockIdx.x;
   uint16_t* out = (uint16_t*)a.out;
   // Shared-prefix decode: sequence s's own pass covers its blocks from
-  // start_block(s) on; the prefix pass has left n_prefix(s) partials for
-  // the blocks before it, which its result folds in.
+  // start_block(s) on (the prefix pass covers those before).
   auto start_block = [&](int s, int nb) {
     if constexpr (SHARED) return min(a.seq_prefix[2 * s], max(nb - 1, 0));
-    else return 0;
-  };
-  auto n_prefix = [&](int s) {
-    if constexpr (SHARED) return a.seq_prefix[2 * s + 1];
     else return 0;
   };
   auto nblocks = [&](int s) {
@@ -199,8 +197,6 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   float* sm_m = smem + NW * g * D;     // [NW][16]
   float* sm_l = sm_m + NW * 16;        // [NW][16]
 
-  const int NS = a.num_splits;
-  int nsp = 0;   // prefix partials of the sequence a piece belongs to
   // One piece: blocks [bb, be) of unit (s, h); piece k of np.
   auto piece = [&](int s, int h, int L, int bb, int be, int k, int np) {
     // Q^T operand: lane (head column col, group grp) holds 8 channels per product.
@@ -307,21 +303,16 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
         acc += sm_o[(v * g + c) * D + dd] * f;
       }
       const int64_t row = (int64_t)s * hq + h * g + c;
-      if (np == 1 && (!SHARED || nsp == 0)) {
-        out[row * D + dd] = f32_to_bf16(acc / lsum);
-      } else if (SHARED && np == 1) {
-        // fold in the prefix pass's partials (log-sum-exp rule, natural log)
-        const float ms = M * kLn2;
-        float Mx = ms;
-        for (int j = 0; j < nsp; ++j) Mx = fmaxf(Mx, a.pre_m[row * NS + j]);
-        float den = lsum * expf(ms - Mx);
-        float num = acc * expf(ms - Mx);   // (acc / lsum) * lsum * e^(ms - Mx)
-        for (int j = 0; j < nsp; ++j) {
-          const float wj = a.pre_l[row * NS + j] * expf(a.pre_m[row * NS + j] - Mx);
-          num = fmaf(wj, a.pre_o[(row * NS + j) * D + dd], num);
-          den += wj;
+      if constexpr (SHARED) {
+        // every piece is a partial; a later kernel merges them with the
+        // prefix pass's partials
+        a.part_o[(row * P + k) * D + dd] = acc / lsum;
+        if (dd == 0) {
+          a.part_m[row * P + k] = M * kLn2;
+          a.part_l[row * P + k] = lsum;
         }
-        out[row * D + dd] = f32_to_bf16(num / den);
+      } else if (np == 1) {
+        out[row * D + dd] = f32_to_bf16(acc / lsum);
       } else {
         put(&a.part_o[(row * P + k) * D + dd], acc / lsum);
         if (dd == 0) {
@@ -330,28 +321,22 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
         }
       }
     }
+    if constexpr (SHARED)
+      if (k == 0 && tid == 0) a.counters[(int64_t)s * hkv + h] = np;   // pieces of the unit
   };
 
   // Merge all np pieces of unit (s, h) (called by the piece that arrived
   // last): the pieces' weights l_j e^(m_j - M) go through LDS (one load per
   // (head, piece) across the workgroup), then every (head, channel) thread
   // sums its o_j with eight loads in flight.
-  // Prefix partials of a shared-prefix decode count as pieces np..np+nsp-1
-  // (written by an earlier kernel: plain loads).
-  auto merge = [&](int s, int h, int np_own, int nsp) {
-    const int np = np_own + nsp;
+  auto merge = [&](int s, int h, int np) {
     float* sw = smem;   // [g][np] m, [g][np] weights, [g] inverse sums
     for (int idx = tid; idx < g * np; idx += NT) {
       const int c = idx / np;
       const int j = idx - c * np;
       const int64_t row = (int64_t)s * hq + h * g + c;
-      if (!SHARED || j < np_own) {
-        sw[idx] = get(&a.part_m[row * P + j]);
-        sw[g * np + idx] = get(&a.part_l[row * P + j]);
-      } else {
-        sw[idx] = a.pre_m[row * NS + j - np_own];
-        sw[g * np + idx] = a.pre_l[row * NS + j - np_own];
-      }
+      sw[idx] = get(&a.part_m[row * P + j]);
+      sw[g * np + idx] = get(&a.part_l[row * P + j]);
     }
     __syncthreads();
     if (tid < g) {
@@ -372,16 +357,14 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
       const int64_t row = (int64_t)s * hq + h * g + c;
       const float* wts = sw + g * np + c * np;
       float acc = 0.f;
-      for (int j0 = 0; j0 < np_own; j0 += 8) {
+      for (int j0 = 0; j0 < np; j0 += 8) {
         float ov[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ov[u] = get(&a.part_o[(row * P + min(j0 + u, np_own - 1)) * D + dd]);
+        for (int u = 0; u < 8; ++u) ov[u] = get(&a.part_o[(row * P + min(j0 + u, np - 1)) * D + dd]);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (j0 + u < np_own) acc = fmaf(wts[j0 + u], ov[u], acc);
+          if (j0 + u < np) acc = fmaf(wts[j0 + u], ov[u], acc);
       }
-      if constexpr (SHARED)
-        for (int j = 0; j < nsp; ++j) acc = fmaf(wts[np_own + j], a.pre_o[(row * NS + j) * D + dd], acc);
       out[row * D + dd] = f32_to_bf16(acc * sw[2 * g * np + c]);
     }
     __syncthreads();   // the LDS is reused by the next merge
@@ -397,7 +380,6 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
     const int nb_all = (L + kBs - 1) / kBs;
     const int st = start_block(s, nb_all);
     const int nb = nb_all - st;
-    nsp = n_prefix(s);
     for (int h = 0; h < hkv; ++h) {
       const int64_t Gh = G + (int64_t)h * nb;
       const int64_t a0 = max(lo, Gh), a1 = min(hi, Gh + nb);
@@ -405,7 +387,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
         const int k = (int)(w - Gh / C);
         const int np = (int)((Gh + nb - 1) / C - Gh / C + 1);
         piece(s, h, L, st + (int)(a0 - Gh), st + (int)(a1 - Gh), k, np);
-        if (np > 1 && n_pend < 2) {
+        if (!SHARED && np > 1 && n_pend < 2) {
           pend_s[n_pend] = s;
           pend_h[n_pend] = h;
           pend_np[n_pend] = np;
@@ -434,7 +416,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   }
   __syncthreads();
   for (int i = 0; i < n_pend; ++i)
-    if (sh_lastv[i]) merge(pend_s[i], pend_h[i], pend_np[i], n_prefix(pend_s[i]));
+    if (sh_lastv[i]) merge(pend_s[i], pend_h[i], pend_np[i]);
 }
 
 // ---------------------------------------------------------------- fp32 pass 1
@@ -605,6 +587,60 @@ __global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* c, int64_t
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) c[i] = 0;
 }
 
+// Shared-prefix decode, last step: for every (sequence, KV head) the pieces
+// of the sequence's own pass and the prefix pass's partials are combined by
+// the log-sum-exp rule, out = sum_j o_j l_j e^(m_j - M) / sum_j l_j e^(m_j - M)
+// (natural-log statistics).  A unit whose context is empty (piece count 0)
+// was given its zero rows by the decode kernel.
+template <int D>
+__global__ __launch_bounds__(256) void decode_fold_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float fold_s[];   // [g][n] m, [g][n] weights, [g] 1/sum
+  const int hkv = a.num_kv_heads;
+  const int hq = a.num_q_heads;
+  const int g = hq / hkv;
+  const int unit = blockIdx.x;
+  const int s = unit / hkv;
+  const int h = unit - s * hkv;
+  const int np = a.counters[unit];
+  if (np <= 0) return;
+  const int NS = a.num_splits;
+  const int P = a.max_partitions;
+  const int nsp = min(max(a.seq_prefix[2 * s + 1], 0), NS);
+  const int n = np + nsp;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < g * n; idx += 256) {
+    const int c = idx / n;
+    const int j = idx - c * n;
+    const int64_t row = (int64_t)s * hq + h * g + c;
+    fold_s[idx] = j < np ? a.part_m[row * P + j] : a.pre_m[row * NS + j - np];
+    fold_s[g * n + idx] = j < np ? a.part_l[row * P + j] : a.pre_l[row * NS + j - np];
+  }
+  __syncthreads();
+  if (tid < g) {
+    float M = -INFINITY;
+    for (int j = 0; j < n; ++j) M = fmaxf(M, fold_s[tid * n + j]);
+    float wsum = 0.f;
+    for (int j = 0; j < n; ++j) {
+      const float wt = fold_s[g * n + tid * n + j] * expf(fold_s[tid * n + j] - M);
+      fold_s[g * n + tid * n + j] = wt;
+      wsum += wt;
+    }
+    fold_s[2 * g * n + tid] = 1.f / wsum;
+  }
+  __syncthreads();
+  uint16_t* out = (uint16_t*)a.out;
+  for (int idx = tid; idx < g * D; idx += 256) {
+    const int c = idx / D;
+    const int dd = idx - c * D;
+    const int64_t row = (int64_t)s * hq + h * g + c;
+    const float* wts = fold_s + g * n + c * n;
+    float acc = 0.f;
+    for (int j = 0; j < np; ++j) acc = fmaf(wts[j], a.part_o[(row * P + j) * D + dd], acc);
+    for (int j = 0; j < nsp; ++j) acc = fmaf(wts[np + j], a.pre_o[(row * NS + j) * D + dd], acc);
+    out[row * D + dd] = f32_to_bf16(acc * fold_s[2 * g * n + c]);
+  }
+}
+
 template <int D>
 int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
   const int g = a.num_q_heads / a.num_kv_heads;
@@ -612,8 +648,10 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     constexpr int NW = 8;
     // wave-merge area [NW][g][D] + [NW][16] m + [NW][16] l, also used for
     // the piece weights of a merge ([2][g][P] + [g])
-    const size_t words =
-        (size_t)max(NW * g * D + 2 * NW * 16, 2 * g * (a.max_partitions + a.num_splits) + g);
+    // (the shared-prefix variant merges in a separate kernel)
+    const size_t wave_area = (size_t)NW * g * D + 2 * NW * 16;
+    const size_t merge_area = (size_t)2 * g * a.max_partitions + g;
+    const size_t words = a.seq_prefix ? wave_area : max(wave_area, merge_area);
     const size_t lds = words * sizeof(float);
     if (lds > kDecodeLdsMax) return -2;
     auto kern = a.seq_prefix ? decode_bf16_kernel<D, NW, true> : decode_bf16_kernel<D, NW, false>;
@@ -630,6 +668,21 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
       clear_counters_kernel<<<(int)(cgrid < 1024 ? (cgrid > 0 ? cgrid : 1) : 1024), 256, 0, st>>>(
           a.counters, units);
     kern<<<a.num_workgroups, NW * kWave, lds, st>>>(a);
+    if (a.seq_prefix) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return -4;
+      const size_t flds = (size_t)(2 * g * (a.max_partitions + a.num_splits) + g) * sizeof(float);
+      if (flds > kDecodeLdsMax) return -2;
+      static bool fold_attr = false;
+      if (!fold_attr) {
+        if (hipFuncSetAttribute((const void*)decode_fold_kernel<D>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)kDecodeLdsMax) != hipSuccess)
+          return -4;
+        fold_attr = true;
+      }
+      decode_fold_kernel<D><<<(unsigned)units, 256, flds, st>>>(a);
+    }
     return status_of(hipGetLastError());
   }
   const int n_part = a.max_partitions - 1;   // fixed partitions of the fp32 path
