@@ -40,7 +40,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak
 METRIC = "paged decode HBM GB/s (% of peak) and tokens/s at Llama-3-8B GQA shape"
 
-WORKLOADS = ("gqa4-decode", "long-context-decode", "shared-prefix-decode", "multiturn-extend")
+WORKLOADS = ("gqa4-decode", "long-context-decode", "shared-prefix-decode", "multiturn-extend",
+             "swap-host")
 
 
 def parse():
@@ -63,7 +64,7 @@ def parse():
 # ---------------------------------------------------------------- workloads
 def make_case(name, total_steps):
     import workloads as W
-    if name == "gqa4-decode":
+    if name in ("gqa4-decode", "swap-host"):
         return W.gqa4_decode(spare_blocks=64 * (total_steps // 16 + 2))
     if name == "long-context-decode":
         # the long-context workload's draws (seed 3), with room for the decode steps
@@ -407,6 +408,68 @@ def run_shared(args, case, torch, lib, alloc_cls):
                 cow_pairs=n_pairs, shared=groups is not None)
 
 
+def run_swap(args, case, torch, lib, alloc_cls):
+    """The gqa4 decode case's whole KV cache moved to pinned host memory and
+    back: one step = swap_out of all 64 sequences + swap_blocks (device ->
+    host), then swap_in + swap_blocks (host -> device).  A pinned DMA copy
+    of the same byte count (torch copy_) is timed beside it as the link's
+    practical rate."""
+    dev = torch.device("cuda:0")
+    S, hkv, d = case.num_seqs, case.num_kv_heads, case.head_dim
+    nb = case.num_blocks
+    alloc = alloc_cls(nb, 16, max_seqs=S, free_order=case.free_order, num_host_blocks=nb)
+    sids = [alloc.new_seq() for _ in range(S)]
+    slots = np.concatenate([alloc.append_tokens(s, int(L))[0] for s, L in zip(sids, case.context_lens)])
+    k_pool, v_pool = lib.new_pools(nb, hkv, d, 16, torch.bfloat16, dev)
+    lib.paged_kv_append(torch.from_numpy(case.k.view(np.int16)).view(torch.bfloat16).to(dev),
+                        torch.from_numpy(case.v.view(np.int16)).view(torch.bfloat16).to(dev),
+                        torch.from_numpy(slots).to(dev), k_pool, v_pool)
+    hk, hv = lib.new_host_pools(nb, hkv, d, 16, torch.bfloat16)
+    blk_bytes = 2 * hkv * 16 * d * 2
+    outs, ins, moved = [], [], []
+    T = args.warmup + args.steps
+    torch.cuda.synchronize()
+    t0 = None
+    for i in range(T):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        pairs = torch.from_numpy(alloc.swap_out(sids)).to(dev)
+        e[0].record()
+        lib.swap_blocks(hk, hv, k_pool, v_pool, pairs)
+        e[1].record()
+        pairs = torch.from_numpy(alloc.swap_in(sids)).to(dev)
+        e[2].record()
+        lib.swap_blocks(k_pool, v_pool, hk, hv, pairs)
+        e[3].record()
+        if i >= args.warmup:
+            outs.append((e[0], e[1]))
+            ins.append((e[2], e[3]))
+            moved.append(len(pairs) * blk_bytes)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    alloc.validate()
+    # reference: one pinned DMA copy each way of the same bytes
+    n = moved[0]
+    h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    g = torch.empty(n, dtype=torch.uint8, device=dev)
+    ref = {}
+    for name, (dst, src) in (("d2h", (h, g)), ("h2d", (g, h))):
+        ts = []
+        for _ in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.copy_(src, non_blocking=True)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        ref[name] = n / float(np.median(ts[1:])) / 1e9
+    d_out = [a.elapsed_time(b) * 1e-3 for a, b in outs]
+    d_in = [a.elapsed_time(b) * 1e-3 for a, b in ins]
+    return dict(elapsed=el, moved=moved, d_out=d_out, d_in=d_in, ref=ref)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -439,6 +502,30 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    if args.workload == "swap-host":
+        r = run_swap(args, case, torch, lib, BlockAllocator)
+        per = float(np.mean(r["moved"]))
+        go, gi = per / np.mean(r["d_out"]) / 1e9, per / np.mean(r["d_in"]) / 1e9
+        line = {"metric": "KV block swap GB/s, device pool <-> pinned host pool (whole cache "
+                          "of the gqa4 decode workload, both directions)",
+                "value": round(2 * per * args.steps / r["elapsed"] / 1e9, 2), "unit": "GB/s",
+                "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(r["elapsed"] / args.steps * 1e3, 3),
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "bf16", "data": "synthetic (the gqa4 decode workload's pool)",
+                "config": {"workload": "swap-host", "blocks_per_direction": int(per // (2 * 8 * 16 * 128 * 2)),
+                           "bytes_per_direction": int(per)},
+                "roofline": {"bound": "host-link", "achieved": round(min(go, gi), 1),
+                             "peak": round(min(r["ref"]["d2h"], r["ref"]["h2d"]), 1),
+                             "unit": "GB/s", "frac": round(min(go / r["ref"]["d2h"], gi / r["ref"]["h2d"]), 4),
+                             "traffic": None, "kernel": "swap_blocks (swap_blocks_kernel)",
+                             "d2h_gbps": round(go, 1), "h2d_gbps": round(gi, 1),
+                             "peak_is": "pinned DMA copy of the same bytes (torch copy_), measured",
+                             "dma_d2h_gbps": round(r["ref"]["d2h"], 1),
+                             "dma_h2d_gbps": round(r["ref"]["h2d"], 1)},
+                "cpu_baseline": None}
+        print(json.dumps(line), flush=True)
+        return
     if args.workload == "multiturn-extend":
         r = run_extend(args, case, torch, lib, BlockAllocator)
         kern = ["extend.hip"]

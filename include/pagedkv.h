@@ -112,6 +112,31 @@ int copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks,
                 int32_t dtype, void* stream);
 
 /*
+ * swap_blocks -- copy whole blocks (K and V) from one pool to another, where
+ * either pool may live in pinned host memory: the tier below HBM, for blocks
+ * moved out of the GPU and back ("PagedAttention and RadixAttention: Let's
+ * Talk About KV Cache", section "Beyond the Two Techniques", hierarchical
+ * memory: hot blocks in GPU memory, recently used ones in host RAM).
+ *
+ *   dst_k, dst_v   [dst_num_blocks][num_kv_heads][block_size][head_dim] pools
+ *                  (the pool layout of paged_kv_append), written
+ *   src_k, src_v   [src_num_blocks][...] pools, read
+ *   block_mapping  [num_pairs][2] int32, device memory: (src block, dst block)
+ *
+ * Each pool is device memory or pinned host memory (hipHostMalloc, or a
+ * pinned torch tensor); host pools are accessed through their device
+ * mapping by the copy kernel, so the call is asynchronous on stream like the
+ * others.  Bit-exact.  Pairs with a block id out of range are skipped;
+ * destination blocks should be distinct (if not, which copy wins is
+ * unspecified).  PKV_ERR_INVALID for memory that is neither device memory
+ * nor pinned host memory.
+ */
+int swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* src_k,
+                const void* src_v, int32_t src_num_blocks, const int32_t* block_mapping,
+                int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t dtype, void* stream);
+
+/*
  * Size in bytes of the workspace paged_attention_decode needs for these
  * arguments; partition_size as in paged_attention_decode (0 = the library's
  * choice).  Returns 0 only for invalid arguments (the decode call reports

@@ -106,3 +106,92 @@ class RefBlockManager:
 
     def table(self, sid: int):
         return list(self.tables[sid])
+
+
+class SwapBlockManager(RefBlockManager):
+    """The block manager plus a host tier: a group of sequences can be moved
+    out of the device pool into host blocks and back ("PagedAttention and
+    RadixAttention: Let's Talk About KV Cache", "Beyond the Two Techniques":
+    hot blocks in GPU memory, recently used ones in host RAM).
+
+    Rules fixed here (the library follows them):
+
+    * A move takes a set of sequences; every block they reference, in the
+      order first met (sequences in the order given, then logical order), gets
+      one block of the other tier, taken first-in first-out from that tier's
+      free list, with the same reference count.  Their tables are rewritten;
+      the old blocks return to their free list in that same order.
+    * A block also referenced by a sequence outside the set cannot move
+      (ValueError); too few free blocks in the other tier raise OutOfBlocks.
+      Either leaves the state unchanged.
+    * A sequence on the host tier takes no appends or forks until it is moved
+      back.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None, num_host_blocks=0):
+        super().__init__(num_blocks, block_size, free_order)
+        self.host_free = deque(range(num_host_blocks))
+        self.host_ref = {}
+        self.on_host = set()
+
+    def _move(self, sids, to_host: bool):
+        src_ref = self.ref if to_host else self.host_ref
+        dst_ref = self.host_ref if to_host else self.ref
+        src_free = self.free if to_host else self.host_free
+        dst_free = self.host_free if to_host else self.free
+        blocks = []
+        for s in sids:
+            if (s in self.on_host) == to_host:
+                raise ValueError("sequence already on that tier")
+            for b in self.tables[s]:
+                if b not in blocks:
+                    blocks.append(b)
+        for b in blocks:
+            inside = sum(self.tables[s].count(b) for s in sids)
+            if inside != src_ref[b]:
+                raise ValueError("a block is shared with a sequence outside the set")
+        if len(blocks) > len(dst_free):
+            raise OutOfBlocks("the other tier has too few free blocks")
+        new = {}
+        for b in blocks:
+            new[b] = dst_free.popleft()
+            dst_ref[new[b]] = src_ref[b]
+        for s in sids:
+            self.tables[s] = [new[b] for b in self.tables[s]]
+            if to_host:
+                self.on_host.add(s)
+            else:
+                self.on_host.discard(s)
+        for b in blocks:
+            del src_ref[b]
+            src_free.append(b)
+        return [(b, new[b]) for b in blocks]
+
+    def swap_out(self, sids):
+        """Move the sequences to the host tier; returns (device, host) pairs."""
+        return self._move(list(sids), True)
+
+    def swap_in(self, sids):
+        """Move them back; returns (host, device) pairs."""
+        return self._move(list(sids), False)
+
+    def append(self, sid, n):
+        if sid in self.on_host:
+            raise ValueError("sequence is on the host tier")
+        return super().append(sid, n)
+
+    def fork(self, sid):
+        if sid in self.on_host:
+            raise ValueError("sequence is on the host tier")
+        return super().fork(sid)
+
+    def free_seq(self, sid):
+        if sid not in self.on_host:
+            return super().free_seq(sid)
+        for b in self.tables.pop(sid):
+            self.host_ref[b] -= 1
+            if self.host_ref[b] == 0:
+                del self.host_ref[b]
+                self.host_free.append(b)
+        del self.lens[sid]
+        self.on_host.discard(sid)

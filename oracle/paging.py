@@ -93,6 +93,20 @@ def copy_blocks(k_pool, v_pool, block_mapping) -> None:
         v_pool[dst] = v_before[src]
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping) -> None:
+    """Move whole blocks between two pools (device and host tiers): each
+    ``dst`` block of the destination pools becomes an exact copy of its
+    ``src`` block of the source pools, K and V, all heads and slots.
+
+    "PagedAttention and RadixAttention: Let's Talk About KV Cache", section
+    "Beyond the Two Techniques": blocks move between GPU memory and host RAM
+    and come back when needed; a block's contents travel unchanged.
+    """
+    for src, dst in np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2):
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+
+
 def gather(k_pool, v_pool, table_row, context_len: int, block_size: int):
     """Follow one sequence's block table and return its keys and values in
     logical order, as ``[context_len][num_kv_heads][head_dim]`` raw words.

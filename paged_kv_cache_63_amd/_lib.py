@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 _LIB = None
 
 PKV_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
-SYMBOLS = ("paged_kv_append", "copy_blocks", "paged_attention_decode_workspace_size",
+SYMBOLS = ("paged_kv_append", "copy_blocks", "swap_blocks", "paged_attention_decode_workspace_size",
            "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
            "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
            "paged_kv_last_error")
@@ -45,6 +45,8 @@ def load():
     lib.paged_kv_append.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, i32, p]
     lib.copy_blocks.restype = ctypes.c_int
     lib.copy_blocks.argtypes = [p, p, i32, p, i32, i32, i32, i32, i32, p]
+    lib.swap_blocks.restype = ctypes.c_int
+    lib.swap_blocks.argtypes = [p, p, i32, p, p, i32, p, i32, i32, i32, i32, i32, p]
     lib.paged_attention_decode_workspace_size.restype = sz
     lib.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_attention_decode.restype = ctypes.c_int
@@ -92,7 +94,13 @@ def _int32(*ts):
             raise ValueError("index tensors must be int32")
 
 
-def _pools(k_pool, v_pool):
+def _pools(k_pool, v_pool, host_ok=False):
+    for t in (k_pool, v_pool):
+        if not t.is_contiguous():
+            raise ValueError("pools must be contiguous")
+        if not t.is_cuda and not (host_ok and t.is_pinned()):
+            raise ValueError("pools must be on the GPU" + (" or in pinned host memory"
+                                                            if host_ok else ""))
     if k_pool.dim() != 4 or v_pool.dim() != 4:
         raise ValueError("pools must be 4-D")
     nb, hkv, bs, d = k_pool.shape
@@ -133,6 +141,32 @@ def copy_blocks(k_pool, v_pool, block_mapping):
         raise ValueError("block_mapping must be [N][2]")
     _check(load().copy_blocks(_ptr(k_pool), _ptr(v_pool), nb, _ptr(block_mapping),
                               block_mapping.shape[0], hkv, d, bs, dt, _stream()))
+
+
+def new_host_pools(num_blocks, num_kv_heads, head_dim, block_size=16, dtype=torch.bfloat16):
+    """Pinned host pools with the device pools' layout (the host tier for
+    :func:`swap_blocks`)."""
+    return (torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype,
+                        pin_memory=True),
+            torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype,
+                        pin_memory=True))
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping):
+    """Copy blocks ``block_mapping[i] = (src, dst)`` from the (src_k, src_v)
+    pools into the (dst_k, dst_v) pools; either pair may be pinned host
+    pools.  Runs on torch's current stream."""
+    dnb, hkv, bs, d, dt = _pools(dst_k, dst_v, host_ok=True)
+    snb, hkv2, bs2, d2, dt2 = _pools(src_k, src_v, host_ok=True)
+    if (hkv, bs, d, dt) != (hkv2, bs2, d2, dt2):
+        raise ValueError("source and destination pools differ in shape or dtype")
+    _dev(block_mapping)
+    _int32(block_mapping)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n][2]")
+    _check(load().swap_blocks(_ptr(dst_k), _ptr(dst_v), dnb, _ptr(src_k), _ptr(src_v), snb,
+                              _ptr(block_mapping), block_mapping.shape[0], hkv, d, bs, dt,
+                              _stream()))
 
 
 def paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,

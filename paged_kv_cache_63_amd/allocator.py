@@ -53,7 +53,7 @@ def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int,
 
 class BlockAllocator:
     def __init__(self, num_blocks: int, block_size: int = 16, max_seqs: int = 256,
-                 max_blocks_per_seq: int = None, free_order=None):
+                 max_blocks_per_seq: int = None, free_order=None, num_host_blocks: int = 0):
         if num_blocks <= 0 or block_size <= 0 or max_seqs <= 0:
             raise ValueError("num_blocks, block_size and max_seqs must be positive")
         self.num_blocks = int(num_blocks)
@@ -73,6 +73,11 @@ class BlockAllocator:
             raise ValueError("free_order must be a permutation of range(num_blocks)")
         self._free = deque(int(b) for b in order)
         self._rows = deque(range(self.max_seqs))
+        # host tier: blocks of sequences moved out of the device pool
+        self.num_host_blocks = int(num_host_blocks)
+        self.host_ref = np.zeros(self.num_host_blocks, dtype=np.int32)
+        self._host_free = deque(range(self.num_host_blocks))
+        self.on_host = np.zeros(self.max_seqs, dtype=bool)
 
     # ---------------------------------------------------------------- blocks
     def _take(self, n: int) -> np.ndarray:
@@ -155,6 +160,11 @@ class BlockAllocator:
         if not (0 <= sid < self.max_seqs) or not self.live[sid]:
             raise KeyError(f"sequence {sid} is not live")
 
+    def _check_dev(self, sid: int) -> None:
+        self._check(sid)
+        if self.on_host[sid]:
+            raise ValueError(f"sequence {sid} is on the host tier (swap it in first)")
+
     def append_tokens(self, sid: int, n: int):
         """Reserve slots for ``n`` more tokens of one sequence.
 
@@ -162,7 +172,7 @@ class BlockAllocator:
         new token, in order, and the copy-on-write pairs that must be copied
         on the device before the tokens are written.
         """
-        self._check(sid)
+        self._check_dev(sid)
         B = self.block_size
         pos0 = int(self.lens[sid])
         nb = int(self.nblk[sid])
@@ -207,6 +217,8 @@ class BlockAllocator:
             raise ValueError("a sequence may appear once per step")
         if not self.live[sids].all():
             raise KeyError("append_step on a sequence that is not live")
+        if self.on_host[sids].any():
+            raise ValueError("append_step on a sequence on the host tier")
         B = self.block_size
         pos = self.lens[sids].astype(np.int64)
         nb = self.nblk[sids].astype(np.int64)
@@ -271,7 +283,7 @@ class BlockAllocator:
 
     def fork(self, sid: int, n: int = 1):
         """``n`` new sequences sharing every block of ``sid`` by reference."""
-        self._check(sid)
+        self._check_dev(sid)
         if n > len(self._rows):
             raise RuntimeError("no free sequence row (max_seqs reached)")
         nb = int(self.nblk[sid])
@@ -289,7 +301,7 @@ class BlockAllocator:
         """Drop the sequence's tokens from ``new_len`` on (a rejected draft, a
         re-run chunk).  Blocks no longer needed lose this sequence's reference
         and, at zero, return to the back of the free list in logical order."""
-        self._check(sid)
+        self._check_dev(sid)
         if not 0 <= new_len <= int(self.lens[sid]):
             raise ValueError("new_len must be within the current length")
         nb = int(self.nblk[sid])
@@ -307,13 +319,80 @@ class BlockAllocator:
         self._check(sid)
         nb = int(self.nblk[sid])
         blocks = self.tables[sid, :nb].copy()
-        self.ref[blocks] -= 1
-        self._release(blocks[self.ref[blocks] == 0])
+        if self.on_host[sid]:
+            for b in blocks:
+                self.host_ref[b] -= 1
+                if self.host_ref[b] == 0:
+                    self._host_free.append(int(b))
+            self.on_host[sid] = False
+        else:
+            self.ref[blocks] -= 1
+            self._release(blocks[self.ref[blocks] == 0])
         self.tables[sid] = -1
         self.lens[sid] = 0
         self.nblk[sid] = 0
         self.live[sid] = False
         self._rows.append(sid)
+
+    # ------------------------------------------------------------ host tier
+    def _move(self, sids, to_host: bool) -> np.ndarray:
+        sids = [int(x) for x in sids]
+        for x in sids:
+            self._check(x)
+            if bool(self.on_host[x]) == to_host:
+                raise ValueError(f"sequence {x} is already on that tier")
+        if len(set(sids)) != len(sids):
+            raise ValueError("a sequence may appear once")
+        rows = [self.tables[x, :self.nblk[x]] for x in sids]
+        cat = np.concatenate(rows) if rows else np.zeros(0, np.int32)
+        blocks, first = np.unique(cat, return_index=True)
+        blocks = blocks[np.argsort(first)]               # in the order first met
+        inside = np.zeros(len(blocks), dtype=np.int64)
+        pos = {int(b): i for i, b in enumerate(blocks)}
+        for b in cat:
+            inside[pos[int(b)]] += 1
+        src_ref = self.ref if to_host else self.host_ref
+        if len(blocks) and (src_ref[blocks] != inside).any():
+            raise ValueError("a block is shared with a sequence outside the set")
+        avail = len(self._host_free) if to_host else self._available()
+        if len(blocks) > avail:
+            raise OutOfBlocks(f"need {len(blocks)} blocks on the other tier, {avail} free")
+        if to_host:
+            new = np.fromiter((self._host_free.popleft() for _ in range(len(blocks))),
+                              dtype=np.int32, count=len(blocks))
+            self.host_ref[new] = src_ref[blocks]
+        else:
+            new = self._take(len(blocks))
+            self.ref[new] = src_ref[blocks]
+        remap = dict(zip(blocks.tolist(), new.tolist()))
+        for x in sids:
+            nb = int(self.nblk[x])
+            self.tables[x, :nb] = [remap[int(b)] for b in self.tables[x, :nb]]
+            self.on_host[x] = to_host
+        src_ref[blocks] = 0
+        if to_host:
+            self._release(blocks)
+        else:
+            self._host_free.extend(int(b) for b in blocks)
+        return np.stack([blocks, new], axis=1).astype(np.int32) if len(blocks) else \
+            np.zeros((0, 2), dtype=np.int32)
+
+    def swap_out(self, sids) -> np.ndarray:
+        """Move the sequences' blocks to the host tier.  Every block they
+        reference, in the order first met, gets a host block (first-in
+        first-out) with the same reference count; their tables now name host
+        blocks and the device blocks return to the free list in that order.
+        Returns ``(device block, host block)`` pairs for :func:`swap_blocks`.
+        A block shared with a sequence outside the set raises ValueError; too
+        few host blocks raise OutOfBlocks; either leaves the state unchanged."""
+        return self._move(sids, True)
+
+    def swap_in(self, sids) -> np.ndarray:
+        """The inverse move; returns ``(host block, device block)`` pairs."""
+        return self._move(sids, False)
+
+    def num_free_host(self) -> int:
+        return len(self._host_free)
 
     # --------------------------------------------------------------- queries
     def context_len(self, sid: int) -> int:
@@ -331,6 +410,7 @@ class BlockAllocator:
         ``held``: references per block held outside sequence tables (a prefix
         tree's), if any."""
         count = np.zeros(self.num_blocks, dtype=np.int64)
+        hcount = np.zeros(self.num_host_blocks, dtype=np.int64)
         if held is not None:
             count += held
         for sid in np.flatnonzero(self.live):
@@ -340,8 +420,17 @@ class BlockAllocator:
             assert (self.tables[sid, nb:] == -1).all(), "table padding"
             assert len(np.unique(row)) == nb, "block repeated within a sequence"
             assert 0 <= self.waste(sid) < self.block_size or nb == 0, "waste bound"
-            count[row] += 1
+            if self.on_host[sid]:
+                hcount[row] += 1
+            else:
+                count[row] += 1
         assert (count + self._holders() == self.ref).all(), "refcount != number of references"
+        assert (hcount == self.host_ref).all(), "host refcount != number of references"
+        hfree = np.array(list(self._host_free), dtype=np.int64)
+        assert len(np.unique(hfree)) == len(hfree) and (self.host_ref[hfree] == 0).all(), \
+            "host free list"
+        assert len(hfree) + int((self.host_ref > 0).sum()) == self.num_host_blocks, \
+            "host block leaked"
         free = np.array(list(self._free) + list(self._idle()), dtype=np.int64)
         assert len(np.unique(free)) == len(free), "block twice on the free list"
         assert (self.ref[free] == 0).all(), "referenced block on the free list"

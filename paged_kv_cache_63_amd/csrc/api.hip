@@ -111,6 +111,26 @@ SharedLayout shared_layout(int64_t S, int64_t hq, int64_t hkv, int64_t D, int64_
   return l;
 }
 
+// The address a kernel uses for p: p itself for device memory, the device
+// mapping for pinned host memory.  Non-zero for memory HIP does not know.
+int device_view(const void* p, void** out) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    if (!at.devicePointer) return 1;
+    *out = (uint8_t*)at.devicePointer + ((const uint8_t*)p - (const uint8_t*)at.hostPointer);
+    return 0;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *out = const_cast<void*>(p);
+    return 0;
+  }
+  return 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,6 +166,30 @@ int copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, const int32_t* b
   rc = pkv::launch_copy_blocks(k_pool, v_pool, num_blocks, block_mapping, num_pairs, num_kv_heads,
                                head_dim, block_size, elem_bytes(dtype), (hipStream_t)stream);
   return rc ? fail(rc, "copy_blocks launch failed") : ok();
+}
+
+int swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* src_k,
+                const void* src_v, int32_t src_num_blocks, const int32_t* block_mapping,
+                int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t dtype, void* stream) {
+  int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
+  if (rc) return rc;
+  if (num_pairs < 0 || dst_num_blocks <= 0 || src_num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "bad num_pairs/num_blocks");
+  if (num_pairs == 0) return ok();
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_mapping)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  void* dk = nullptr;
+  void* dv = nullptr;
+  void* sk = nullptr;
+  void* sv = nullptr;
+  if (device_view(dst_k, &dk) || device_view(dst_v, &dv) || device_view(src_k, &sk) ||
+      device_view(src_v, &sv))
+    return fail(PKV_ERR_INVALID, "pools must be device memory or pinned host memory");
+  rc = pkv::launch_swap_blocks(dk, dv, dst_num_blocks, sk, sv, src_num_blocks, block_mapping,
+                               num_pairs, num_kv_heads, head_dim, block_size, elem_bytes(dtype),
+                               (hipStream_t)stream);
+  return rc ? fail(rc, "swap_blocks launch failed") : ok();
 }
 
 int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,

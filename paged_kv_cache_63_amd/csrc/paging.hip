@@ -73,6 +73,44 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   }
 }
 
+// Block copy between two pools (one of them may be pinned host memory, seen
+// through its device mapping): every (pair, 16-byte piece) of the K and V
+// blocks, grid-stride; each thread has kSwapU pieces of K and of V in flight
+// before it stores any (host-link reads have long latency).
+constexpr int kSwapU = 4;
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, const uint8_t* __restrict__ src_k,
+    const uint8_t* __restrict__ src_v, const int32_t* __restrict__ map, int32_t num_src,
+    int32_t num_dst, int64_t block_pieces, int64_t total) {
+  const int64_t step = (int64_t)gridDim.x * kThreads;
+  for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < total; i0 += step * kSwapU) {
+    u32x4 a[kSwapU], b[kSwapU];
+    int64_t so[kSwapU], dof[kSwapU];
+    bool ok[kSwapU];
+#pragma unroll
+    for (int u = 0; u < kSwapU; ++u) {
+      const int64_t i = i0 + u * step;
+      const int64_t pair = i / block_pieces;
+      const int64_t piece = i - pair * block_pieces;
+      const int32_t src = i < total ? map[2 * pair] : -1;
+      const int32_t dst = i < total ? map[2 * pair + 1] : -1;
+      ok[u] = src >= 0 && src < num_src && dst >= 0 && dst < num_dst;
+      so[u] = ((int64_t)(ok[u] ? src : 0) * block_pieces + piece) * 16;
+      dof[u] = ((int64_t)(ok[u] ? dst : 0) * block_pieces + piece) * 16;
+      if (ok[u]) {
+        a[u] = *reinterpret_cast<const u32x4*>(src_k + so[u]);
+        b[u] = *reinterpret_cast<const u32x4*>(src_v + so[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSwapU; ++u)
+      if (ok[u]) {
+        *reinterpret_cast<u32x4*>(dst_k + dof[u]) = a[u];
+        *reinterpret_cast<u32x4*>(dst_v + dof[u]) = b[u];
+      }
+  }
+}
+
 // One thread per 16-byte piece of the output rows [ctx][hkv][d].
 template <int E>
 __global__ __launch_bounds__(kThreads) void gather_kernel(
@@ -147,6 +185,21 @@ int launch_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, const int
   if (gx > 64) gx = 64;
   copy_blocks_kernel<<<dim3(gx, num_pairs), kThreads, 0, st>>>(
       (uint8_t*)k_pool, (uint8_t*)v_pool, mapping, num_blocks, block_bytes);
+  return status_of(hipGetLastError());
+}
+
+int launch_swap_blocks(void* dst_k, void* dst_v, int32_t num_dst, const void* src_k,
+                       const void* src_v, int32_t num_src, const int32_t* mapping,
+                       int32_t num_pairs, int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
+                       hipStream_t st) {
+  if (num_pairs == 0) return 0;
+  const int64_t block_pieces = (int64_t)hkv * bs * d * elem_bytes / 16;
+  const int64_t total = block_pieces * num_pairs;
+  int64_t grid = (total + (int64_t)kThreads * kSwapU - 1) / ((int64_t)kThreads * kSwapU);
+  if (grid > 4096) grid = 4096;
+  swap_blocks_kernel<<<(unsigned)grid, kThreads, 0, st>>>(
+      (uint8_t*)dst_k, (uint8_t*)dst_v, (const uint8_t*)src_k, (const uint8_t*)src_v, mapping,
+      num_src, num_dst, block_pieces, total);
   return status_of(hipGetLastError());
 }
 
