@@ -41,15 +41,16 @@ import numpy as np
 from .allocator import BlockAllocator
 
 
+def _digest(parent: bytes, tok: bytes, extra: bytes) -> bytes:
+    return hashlib.sha256(b"".join((len(parent).to_bytes(8, "little"), parent,
+                                    len(tok).to_bytes(8, "little"), tok,
+                                    len(extra).to_bytes(8, "little"), extra))).digest()
+
+
 def block_hash(parent: bytes, tokens, extra: bytes = b"") -> bytes:
     """Digest naming one full block: SHA-256 of the length-prefixed parent
     digest, token ids (int64 little-endian) and extra bytes."""
-    tok = np.ascontiguousarray(tokens, dtype="<i8").tobytes()
-    h = hashlib.sha256()
-    for part in (parent, tok, extra):
-        h.update(len(part).to_bytes(8, "little"))
-        h.update(part)
-    return h.digest()
+    return _digest(parent, np.ascontiguousarray(tokens, dtype="<i8").tobytes(), extra)
 
 
 class PrefixCachingAllocator(BlockAllocator):
@@ -81,14 +82,13 @@ class PrefixCachingAllocator(BlockAllocator):
         return len(self._free) + len(self._idle_lru)
 
     def _take(self, n: int) -> np.ndarray:
+        k = min(n, len(self._free))
         out = np.empty(n, dtype=np.int32)
-        for i in range(n):
-            if self._free:
-                b = self._free.popleft()
-            else:                               # evict the least recently released
-                b, _ = self._idle_lru.popitem(last=False)
-                del self._block_of[self._digest.pop(b)]
-                self.sealed[b] = False
+        out[:k] = [self._free.popleft() for _ in range(k)]
+        for i in range(k, n):                   # evict the least recently released
+            b, _ = self._idle_lru.popitem(last=False)
+            del self._block_of[self._digest.pop(b)]
+            self.sealed[b] = False
             out[i] = b
         self.ref[out] = 1
         return out
@@ -113,10 +113,12 @@ class PrefixCachingAllocator(BlockAllocator):
 
     # ----------------------------------------------------------- sequences
     def _digests(self, tokens, salt: bytes, count: int, parent: bytes = b"", start: int = 0):
-        B = self.block_size
+        step = self.block_size * 8
+        raw = np.ascontiguousarray(tokens[start * self.block_size:count * self.block_size],
+                                   dtype="<i8").tobytes()
         out = []
-        for k in range(start, count):
-            parent = block_hash(parent, tokens[k * B:(k + 1) * B], salt if k == 0 else b"")
+        for i, k in enumerate(range(start, count)):
+            parent = _digest(parent, raw[i * step:(i + 1) * step], salt if k == 0 else b"")
             out.append(parent)
         return out
 
@@ -131,9 +133,11 @@ class PrefixCachingAllocator(BlockAllocator):
         B = self.block_size
         want = min(max(0, (len(tokens) - 1) // B), self.max_blocks_per_seq)
         chain, hits = [], []
+        step = B * 8
+        raw = np.ascontiguousarray(tokens[:want * B], dtype="<i8").tobytes()
         parent = b""
         for k in range(want):
-            parent = self._digests(tokens, salt, k + 1, parent, k)[0]
+            parent = _digest(parent, raw[k * step:(k + 1) * step], salt if k == 0 else b"")
             b = self._block_of.get(parent)
             if b is None:
                 break
@@ -170,8 +174,9 @@ class PrefixCachingAllocator(BlockAllocator):
             salt = self._salt.get(sid, b"")
             chain += self._digests(tokens, salt, full, chain[-1] if chain else b"", len(chain))
         added = 0
-        for k in range(full):
-            b = int(self.tables[sid, k])
+        row = self.tables[sid, :full]
+        for k in np.flatnonzero(~self.sealed[row]).tolist():   # sealed blocks stay as they are
+            b = int(row[k])
             h = chain[k]
             if not self.sealed[b] and h not in self._block_of:
                 self._block_of[h] = b
