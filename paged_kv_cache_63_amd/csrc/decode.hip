@@ -616,18 +616,24 @@ __global__ __launch_bounds__(256) void decode_fold_kernel(DecodeArgs a) {
     fold_s[g * n + idx] = j < np ? a.part_l[row * P + j] : a.pre_l[row * NS + j - np];
   }
   __syncthreads();
-  if (tid < g) {
+  // weights l_j e^(m_j - M) per head: one wave per head, lanes over pieces
+  const int lane = tid & (kWave - 1);
+  for (int c = tid / kWave; c < g; c += 256 / kWave) {
     float M = -INFINITY;
-    for (int j = 0; j < n; ++j) M = fmaxf(M, fold_s[tid * n + j]);
+    for (int j = lane; j < n; j += kWave) M = fmaxf(M, fold_s[c * n + j]);
+    for (int k = kWave / 2; k > 0; k >>= 1) M = fmaxf(M, __shfl_xor(M, k, kWave));
     float wsum = 0.f;
-    for (int j = 0; j < n; ++j) {
-      const float wt = fold_s[g * n + tid * n + j] * expf(fold_s[tid * n + j] - M);
-      fold_s[g * n + tid * n + j] = wt;
+    for (int j = lane; j < n; j += kWave) {
+      const float wt = fold_s[g * n + c * n + j] * expf(fold_s[c * n + j] - M);
+      fold_s[g * n + c * n + j] = wt;
       wsum += wt;
     }
-    fold_s[2 * g * n + tid] = 1.f / wsum;
+    for (int k = kWave / 2; k > 0; k >>= 1) wsum += __shfl_xor(wsum, k, kWave);
+    if (lane == 0) fold_s[2 * g * n + c] = 1.f / wsum;
   }
   __syncthreads();
+  // Each thread's partial outputs are loaded eight at a time, all in
+  // flight together (one latency per eight partials, not one each).
   uint16_t* out = (uint16_t*)a.out;
   for (int idx = tid; idx < g * D; idx += 256) {
     const int c = idx / D;
@@ -635,8 +641,17 @@ __global__ __launch_bounds__(256) void decode_fold_kernel(DecodeArgs a) {
     const int64_t row = (int64_t)s * hq + h * g + c;
     const float* wts = fold_s + g * n + c * n;
     float acc = 0.f;
-    for (int j = 0; j < np; ++j) acc = fmaf(wts[j], a.part_o[(row * P + j) * D + dd], acc);
-    for (int j = 0; j < nsp; ++j) acc = fmaf(wts[np + j], a.pre_o[(row * NS + j) * D + dd], acc);
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      float ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, n - 1);
+        ov[u] = j < np ? a.part_o[(row * P + j) * D + dd] : a.pre_o[(row * NS + j - np) * D + dd];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < n) acc = fmaf(wts[j0 + u], ov[u], acc);
+    }
     out[row * D + dd] = f32_to_bf16(acc * fold_s[2 * g * n + c]);
   }
 }
