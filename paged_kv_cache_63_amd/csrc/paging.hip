@@ -11,6 +11,7 @@ namespace pkv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBulkTokens = 512;  // appends of at least this many tokens look for full-block runs
 
 // One thread per 16-byte piece of one (token, head) row of k_new/v_new.
 // The key piece is stored as it is (rows are contiguous in the K pool); the
@@ -70,6 +71,178 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     const u32x4 b = *reinterpret_cast<const u32x4*>(v_pool + s0 + i * 16);
     *reinterpret_cast<u32x4*>(k_pool + d0 + i * 16) = a;
     *reinterpret_cast<u32x4*>(v_pool + d0 + i * 16) = b;
+  }
+}
+
+// Does token j start a full-block run: slot % 16 == 0 and the next 15
+// tokens take the following slots of the same block?  The 16 loads are
+// independent so that they are in flight together.
+__device__ __forceinline__ bool full_run_at(const int32_t* slots, int64_t j, int64_t n,
+                                            int32_t num_blocks) {
+  if (j < 0 || j + 16 > n) return false;
+  const int32_t s0 = slots[j];
+  bool ok = s0 >= 0 && s0 < num_blocks * 16 && (s0 & 15) == 0;
+#pragma unroll
+  for (int i = 1; i < 16; ++i) ok &= slots[j + i] == s0 + i;
+  return ok;
+}
+
+// Bulk append (block size 16), one launch in two parts.  Workgroups
+// [0, n_win) take one window of 16 input tokens each and handle the
+// full-block run that starts in it, if any (at most one can): the 16 tokens'
+// key rows are copied as whole rows, and their value rows are staged in LDS
+// in input order and read back transposed, so that every (head, channel) row
+// of the V block leaves as whole 16-byte stores instead of 16 scattered
+// element stores.  In the remaining workgroups each wave takes one token
+// and, unless the token is skipped or inside a full run, writes it as
+// append_kernel does.  Every pool word is written by exactly one thread.
+// Below kBulkTokens tokens (a decode step's one token per sequence) runs are
+// rare and append_kernel alone is faster.
+constexpr int kBulkLds = 32768;   // V staging: [16 tokens][heads of one chunk][D] elements
+constexpr int kWaves = kThreads / 64;
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void append_bulk_kernel(
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, int64_t num_tokens, int64_t n_win, int32_t pieces_per_row,
+    int32_t hkv, int32_t d, int32_t num_blocks, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool) {
+  constexpr int bs = 16;
+  constexpr int kPer = 16 / E;
+  constexpr int kB = 4;                      // loads in flight per thread per batch
+  extern __shared__ __attribute__((aligned(16))) uint8_t vbuf[];
+  const int64_t row_bytes = (int64_t)d * E;
+  if (blockIdx.x < n_win) {
+    const int64_t w0 = (int64_t)blockIdx.x * bs;
+    __shared__ int64_t run_j;
+    if (threadIdx.x < 64) {   // lane i of wave 0 tests a run starting at w0 + i
+      const int i = threadIdx.x;
+      const bool ok = i < bs && full_run_at(slots, w0 + i, num_tokens, num_blocks);
+      const unsigned long long m = __ballot(ok);
+      if (i == 0) run_j = m ? w0 + __ffsll((long long)m) - 1 : -1;
+    }
+    __syncthreads();
+    const int64_t j0 = run_j;
+    if (j0 < 0) return;
+    const int32_t blk = slots[j0] >> 4;
+    const int32_t ppr = pieces_per_row;
+    // K: piece i of the run's input (rows (tok, h), contiguous) goes to row
+    // (h, tok) of the block
+    const uint8_t* ksrc = k_new + j0 * hkv * row_bytes;
+    uint8_t* kblk = k_pool + (int64_t)blk * hkv * bs * row_bytes;
+    const int32_t kpieces = bs * hkv * ppr;
+    for (int32_t b0 = threadIdx.x; b0 < kpieces; b0 += kB * kThreads) {
+      u32x4 r[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int32_t i = b0 + u * kThreads;
+        if (i < kpieces) r[u] = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)i * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int32_t i = b0 + u * kThreads;
+        if (i < kpieces) {
+          const int32_t row = i / ppr, piece = i - row * ppr;
+          const int32_t tok = row / hkv, h = row - tok * hkv;
+          *reinterpret_cast<u32x4*>(kblk + ((int64_t)h * bs + tok) * row_bytes + piece * 16) = r[u];
+        }
+      }
+    }
+    // V: heads in chunks of hc whose [16][hc][D] staging fits kBulkLds
+    const uint8_t* vsrc = v_new + j0 * hkv * row_bytes;
+    const int hc_max = max(1, (int)(kBulkLds / (bs * row_bytes)));
+    for (int h0 = 0; h0 < hkv; h0 += hc_max) {
+      const int hc = min(hc_max, hkv - h0);
+      const int32_t cpr = hc * ppr;          // pieces of one token's chunk
+      const int32_t vpieces = bs * cpr;
+      for (int32_t b0 = threadIdx.x; b0 < vpieces; b0 += kB * kThreads) {
+        u32x4 r[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int32_t i = b0 + u * kThreads;
+          if (i < vpieces) {
+            const int32_t tok = i / cpr, rest = i - tok * cpr;
+            r[u] = *reinterpret_cast<const u32x4*>(vsrc + ((int64_t)tok * hkv + h0) * row_bytes +
+                                                   (int64_t)rest * 16);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int32_t i = b0 + u * kThreads;
+          if (i < vpieces) *reinterpret_cast<u32x4*>(vbuf + (int64_t)i * 16) = r[u];
+        }
+      }
+      __syncthreads();
+      // channel rows out: the element of (token tok, head hl, channel c)
+      // sits at staging index (tok * hc + hl) * d + c; position p of a row
+      // holds token v_pos(p)
+      const uint32_t* w32 = reinterpret_cast<const uint32_t*>(vbuf);
+      uint8_t* vblk = v_pool + ((int64_t)blk * hkv + h0) * d * bs * E;
+      if constexpr (E == 2) {
+        // one task = channels c, c + 1 of one head: one dword per token
+        // holds both, and the two rows are 64 contiguous bytes
+        const int32_t tasks = hc * d / 2;
+        for (int32_t q = threadIdx.x; q < tasks; q += kThreads) {
+          const int32_t hl = q / (d / 2), c = 2 * (q - hl * (d / 2));
+          uint32_t w[bs];
+#pragma unroll
+          for (int p = 0; p < bs; ++p) w[p] = w32[((v_pos(p) * hc + hl) * d + c) >> 1];
+          uint32_t lo[bs / 2], hi[bs / 2];
+#pragma unroll
+          for (int k = 0; k < bs / 2; ++k) {
+            lo[k] = (w[2 * k] & 0xffffu) | (w[2 * k + 1] << 16);
+            hi[k] = (w[2 * k] >> 16) | (w[2 * k + 1] & 0xffff0000u);
+          }
+          u32x4* dst = reinterpret_cast<u32x4*>(vblk + ((int64_t)hl * d + c) * bs * E);
+          dst[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          dst[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+          dst[2] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+          dst[3] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+        }
+      } else {
+        const int32_t tasks = hc * d;        // one task = one channel row
+        for (int32_t q = threadIdx.x; q < tasks; q += kThreads) {
+          const int32_t hl = q / d, c = q - hl * d;
+          uint32_t w[bs];
+#pragma unroll
+          for (int p = 0; p < bs; ++p) w[p] = w32[(v_pos(p) * hc + hl) * d + c];
+          u32x4* dst = reinterpret_cast<u32x4*>(vblk + ((int64_t)hl * d + c) * bs * E);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) dst[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  // one token per wave, outside full runs
+  const int64_t t = (int64_t)(blockIdx.x - n_win) * kWaves + threadIdx.x / 64;
+  if (t >= num_tokens) return;
+  // lane k < 16 tests a run starting at t - 15 + k: all loads in flight together
+  const int lane = threadIdx.x & 63;
+  const bool starts = lane < bs && full_run_at(slots, t - 15 + lane, num_tokens, num_blocks);
+  if (__ballot(starts)) return;
+  const int32_t slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * bs) return;
+  const int32_t blk = slot >> 4, off = slot & 15;
+  const int32_t pieces = hkv * pieces_per_row;
+  for (int32_t i = threadIdx.x % 64; i < pieces; i += 64) {
+    const int32_t h = i / pieces_per_row, piece = i - h * pieces_per_row;
+    const int64_t src = (t * hkv + h) * row_bytes + (int64_t)piece * 16;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + src);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + src);
+    const int64_t head_base = ((int64_t)blk * hkv + h) * bs * row_bytes;
+    *reinterpret_cast<u32x4*>(k_pool + head_base + (int64_t)off * row_bytes + piece * 16) = kv;
+    const int32_t c0 = piece * kPer;
+    uint8_t* vrow = v_pool + head_base + ((int64_t)c0 * bs + v_pos(off)) * E;
+    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if constexpr (E == 2)
+        *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * bs * E) = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+      else
+        *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * bs * E) = w[e];
+    }
   }
 }
 
@@ -165,6 +338,22 @@ int launch_append(const void* k_new, const void* v_new, const int32_t* slots, in
   const int64_t pieces = (int64_t)num_tokens * hkv * ppr;
   if (pieces == 0) return 0;
   const int grid = grid_for(pieces);
+  if (num_tokens >= kBulkTokens && bs == 16) {
+    // full-block runs through LDS, the other tokens one per wave, in one launch
+    const int64_t n_win = (num_tokens + 15) / 16;
+    const int64_t g = n_win + (num_tokens + kWaves - 1) / kWaves;
+    if (g > 0x7fffffff) return -1;
+    const size_t lds = kBulkLds;
+    if (elem_bytes == 2)
+      append_bulk_kernel<2><<<(unsigned)g, kThreads, lds, st>>>(
+          (const uint8_t*)k_new, (const uint8_t*)v_new, slots, num_tokens, n_win, ppr, hkv, d,
+          num_blocks, (uint8_t*)k_pool, (uint8_t*)v_pool);
+    else
+      append_bulk_kernel<4><<<(unsigned)g, kThreads, lds, st>>>(
+          (const uint8_t*)k_new, (const uint8_t*)v_new, slots, num_tokens, n_win, ppr, hkv, d,
+          num_blocks, (uint8_t*)k_pool, (uint8_t*)v_pool);
+    return status_of(hipGetLastError());
+  }
   if (elem_bytes == 2)
     append_kernel<2><<<grid, kThreads, 0, st>>>((const uint8_t*)k_new, (const uint8_t*)v_new, slots,
                                                 pieces, ppr, hkv, d, bs, num_blocks,

@@ -67,6 +67,50 @@ def test_append_skips_negative_slots(gpu):
     assert np.array_equal(after, before)                        # nothing else written
 
 
+def _mixed_run_slots(copies):
+    """Slots for one append that mixes full-block runs with everything that
+    must not be taken for one; ``copies`` repeats the pattern over disjoint
+    blocks (16 per copy), and one more full run ends the input."""
+    s = []
+    for k in range(copies):
+        b = 16 * k
+        s += [(b + 3) * 16 + o for o in range(16)]            # full run, window-aligned
+        s += [(b + 7) * 16 + o for o in range(11, 16)]        # partial tail of a block
+        s += [(b + 2) * 16 + o for o in range(16)]            # full run starting mid-window
+        s += [(b + 5) * 16 + o for o in range(15)]            # 15 consecutive: not a full block
+        s += [-1]                                             # skipped token
+        s += [(b + 9) * 16 + o for o in range(8)]             # two half blocks: broken run
+        s += [(b + 10) * 16 + o for o in range(8, 16)]
+        s += [(b + 11) * 16 + o for o in range(16)]           # full run across two windows
+        s += [(b + 0) * 16 + o for o in range(16)]            # full run
+        s += [(b + 12) * 16 + o for o in (0, 2, 1, 3)]        # right block, wrong order
+        s += [-5, (b + 13) * 16 + 15, (b + 13) * 16]          # scattered single tokens
+    s += [(16 * copies + 1) * 16 + o for o in range(16)]      # full run ending the input
+    return np.asarray(s), 16 * copies + 2
+
+
+@pytest.mark.parametrize("copies", [1, 5], ids=["per-token-path", "bulk-path"])
+@pytest.mark.parametrize("dtype,d,hkv", [("bf16", 128, 8), ("bf16", 64, 3), ("fp32", 128, 2)])
+def test_append_mixed_runs_bit_exact(gpu, dtype, d, hkv, copies):
+    """One call with full-block runs and partial, broken and skipped tokens.
+    Below 512 tokens every token is written on its own; from 512 on, full
+    runs go through the transposed-V path and the rest token by token."""
+    slots, nb = _mixed_run_slots(copies)
+    assert (len(slots) >= 512) == (copies > 1)
+    live = slots[slots >= 0]
+    assert len(np.unique(live)) == len(live)
+    rng = np.random.default_rng(7 + copies)
+    kw = normal_words(rng, (len(slots), hkv, d), dtype)
+    vw = normal_words(rng, (len(slots), hkv, d), dtype)
+    k, v = poisoned_pools(nb, hkv, d, dtype)
+    kp, vp = words_of(k).copy(), words_of(v).copy()
+    _lib.paged_kv_append(to_dev(kw, dtype), to_dev(vw, dtype), i32(slots), k, v)
+    paging.append(kp, vp, kw, vw, slots, 16)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_of(k), kp)
+    assert np.array_equal(words_of(v), vp)
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
 def test_copy_blocks_bit_exact(gpu, dtype, d):
     rng = np.random.default_rng(7)
