@@ -200,7 +200,7 @@ def run_decode(args, case, torch, lib, alloc_cls):
 
     kv_per_tok = 2 * hkv * d * 2
     ev_pairs = []
-    step_bytes = []
+    lens_seen = []
 
     def step(i, timed):
         sl, pairs = alloc.append_step(sids)                                  # a1
@@ -224,9 +224,7 @@ def run_decode(args, case, torch, lib, alloc_cls):
         if timed:
             e1.record()
             ev_pairs.append((e0, e1))
-            ctx = int(alloc.lens[:S].sum())
-            nblk = int(sum(-(-int(x) // 16) for x in alloc.lens[:S]))
-            step_bytes.append(ctx * kv_per_tok + 2 * S * hq * d * 2 + nblk * 4 + S * 4)
+            lens_seen.append(alloc.lens[:S].copy())     # bytes are counted after timing
 
     for i in range(args.warmup):
         step(i, False)
@@ -237,6 +235,8 @@ def run_decode(args, case, torch, lib, alloc_cls):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
+    step_bytes = [int(ln.sum()) * kv_per_tok + 2 * S * hq * d * 2 + int((-(-ln // 16)).sum()) * 4
+                  + S * 4 for ln in lens_seen]
     alloc.validate()
     return dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=step_bytes,
                 ctx_mean=float(alloc.lens[:S].mean()))

@@ -324,6 +324,57 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_
                     int32_t context_len, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t dtype, void* stream);
 
+/*
+ * block_manager_append_step -- HOST call, the one exception to the device
+ * conventions above: every pointer is host memory, nothing is enqueued and
+ * no GPU is touched.  The decode step of the host block manager: one new
+ * token for each sequence in sids, in that order ("Paged Attention for
+ * Efficient Memory Management", The Daily Triptych, "The story" and
+ * technical summary: a token fills the next slot of the sequence's last
+ * block; a full last block is followed by a fresh block from the free pool;
+ * a write into a block that other sequences still reference goes to a
+ * fresh copy, and the last remaining owner writes in place).
+ *
+ * State (the block manager's own arrays, updated in place):
+ *   tables      [max_seqs][max_blocks_per_seq] int32; row = sequence id;
+ *               entries past a sequence's block count are -1
+ *   lens, nblk  [max_seqs] int32: tokens and blocks per sequence
+ *               (nblk = ceil(lens / block_size))
+ *   live, on_host [max_seqs] uint8 (0/1): sequence exists / is on the host tier
+ *   ref         [num_blocks] int32 references per block
+ *   sealed      [num_blocks] uint8 (0/1): contents frozen (a prefix cache
+ *               indexes the block)
+ *   free_ring   [num_blocks] int32 FIFO ring of free block ids
+ *   free_state  [2] int64: head index and count of the ring
+ * Arguments:
+ *   sids        [num_sids] int64 sequence ids, distinct
+ * Results:
+ *   slots_out   [num_sids] int32 slot of each sequence's new token
+ *   pairs_out   [num_sids][2] int32 (src, dst) block copies to make before
+ *               the new tokens are written (copy_blocks); *num_pairs_out of
+ *               them are valid, in sequence order
+ *
+ * A sequence whose last block is full takes the block at the ring's head;
+ * one whose last block has a count above one takes the head block as a
+ * copy destination and drops one count from the old block.  Fresh blocks
+ * are taken in sequence order and get a count of 1.
+ *
+ * Returns PKV_OK; PKV_ERR_INVALID (message set) for a null pointer, bad
+ * sizes, a repeated, out-of-range, dead or host-tier sequence, a table
+ * entry out of range, or a sequence that would exceed max_blocks_per_seq;
+ * PKV_STEP_SEALED if a sequence would write into a sealed block, and
+ * PKV_STEP_SHORT if the step needs more blocks than the ring holds.  On any
+ * return but PKV_OK nothing was changed.
+ */
+#define PKV_STEP_SEALED 1
+#define PKV_STEP_SHORT  2
+int block_manager_append_step(int32_t* tables, int32_t* lens, int32_t* nblk,
+                              const uint8_t* live, const uint8_t* on_host, int32_t max_seqs,
+                              int32_t max_blocks_per_seq, int32_t* ref, const uint8_t* sealed,
+                              int32_t num_blocks, int32_t block_size, const int64_t* sids,
+                              int32_t num_sids, int32_t* free_ring, int64_t* free_state,
+                              int32_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out);
+
 #ifdef __cplusplus
 }
 #endif

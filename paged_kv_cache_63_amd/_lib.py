@@ -22,7 +22,7 @@ PKV_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SYMBOLS = ("paged_kv_append", "copy_blocks", "swap_blocks", "paged_attention_decode_workspace_size",
            "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
            "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
-           "paged_kv_last_error")
+           "paged_kv_last_error", "block_manager_append_step")
 
 
 class PagedKVError(RuntimeError):
@@ -63,6 +63,9 @@ def load():
                                            i32, i32, i32, i32, f32, i32, p]
     lib.paged_kv_gather.restype = ctypes.c_int
     lib.paged_kv_gather.argtypes = [p, p, p, p, i32, p, i32, i32, i32, i32, i32, p]
+    lib.block_manager_append_step.restype = ctypes.c_int
+    lib.block_manager_append_step.argtypes = [p, p, p, p, p, i32, i32, p, p, i32, i32, p, i32,
+                                              p, p, p, p, p]
     _LIB = lib
     return lib
 

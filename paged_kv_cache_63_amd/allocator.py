@@ -9,14 +9,16 @@ RadixAttention", section "PagedAttention"; "PagedAttention and
 RadixAttention: Let's Talk About KV Cache", section "PagedAttention: Memory
 Like an Operating System").
 
-State lives in flat numpy arrays so a decode step over a whole batch is a few
-vector operations:
+State lives in flat numpy arrays, which the library's native decode step
+(``block_manager_append_step``) updates in place for a whole batch:
 
 * ``tables``  int32 ``[max_seqs][max_blocks_per_seq]``; row = sequence id;
   entries past the sequence's block count are ``-1``.  A slice of rows is
   exactly the ``block_tables`` argument the device calls take.
 * ``lens``    int32 ``[max_seqs]`` tokens written per sequence.
 * ``ref``     int32 ``[num_blocks]`` references per physical block.
+* the free list, a FIFO ring of block ids (int32 ``[num_blocks]``) with its
+  head and count in an int64 pair.
 
 Rules where the pages leave a choice (the oracle's block-manager model fixes
 the same ones, and the tests compare the two token for token):
@@ -40,6 +42,75 @@ import numpy as np
 class OutOfBlocks(RuntimeError):
     """Raised when an operation needs more free blocks than the pool has.
     The allocator state is left unchanged."""
+
+
+# Positive returns of block_manager_append_step: nothing was changed.
+_STEP_SEALED = 1    # a sequence would write into a sealed block
+_STEP_SHORT = 2     # the free list holds fewer blocks than the step needs
+_NATIVE = None
+
+
+def _native_step():
+    global _NATIVE
+    if _NATIVE is None:
+        from . import _lib      # imports torch first, then loads the library
+        _NATIVE = _lib.load().block_manager_append_step
+    return _NATIVE
+
+
+def _native_error() -> str:
+    from . import _lib
+    return _lib.load().paged_kv_last_error().decode()
+
+
+class _BlockFifo:
+    """FIFO of free block ids: a ring (``ring`` int32) whose head index and
+    count sit in ``state`` (int64 ``[2]``), where native code can update
+    them.  Capacity: every block of the pool once."""
+
+    def __init__(self, capacity: int, items=()):
+        self.ring = np.zeros(max(int(capacity), 1), dtype=np.int32)
+        self.state = np.zeros(2, dtype=np.int64)
+        self.extend(items)
+
+    def __len__(self) -> int:
+        return int(self.state[1])
+
+    def _index(self, start: int, n: int) -> np.ndarray:
+        return (start + np.arange(n)) % len(self.ring)
+
+    def popleft_n(self, n: int) -> np.ndarray:
+        head, count = int(self.state[0]), int(self.state[1])
+        if n > count:
+            raise IndexError("pop from a short free list")
+        out = self.ring[self._index(head, n)]
+        self.state[0] = (head + n) % len(self.ring)
+        self.state[1] = count - n
+        return out
+
+    def popleft(self) -> int:
+        return int(self.popleft_n(1)[0])
+
+    def extend(self, blocks) -> None:
+        arr = np.asarray(blocks if isinstance(blocks, np.ndarray) else list(blocks),
+                         dtype=np.int32).reshape(-1)
+        head, count = int(self.state[0]), int(self.state[1])
+        if count + len(arr) > len(self.ring):
+            raise ValueError("free list over capacity (a block freed twice)")
+        self.ring[self._index(head + count, len(arr))] = arr
+        self.state[1] = count + len(arr)
+
+    def append(self, block: int) -> None:
+        self.extend([block])
+
+    def __iter__(self):
+        return iter(self.ring[self._index(int(self.state[0]), len(self))].tolist())
+
+    def copy(self) -> "_BlockFifo":
+        c = _BlockFifo.__new__(_BlockFifo)
+        c.ring = self.ring.copy()
+        c.state = self.state.copy()
+        return c
 
 
 def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int,
@@ -71,18 +142,20 @@ class BlockAllocator:
         order = np.arange(self.num_blocks) if free_order is None else np.asarray(free_order)
         if sorted(int(b) for b in order) != list(range(self.num_blocks)):
             raise ValueError("free_order must be a permutation of range(num_blocks)")
-        self._free = deque(int(b) for b in order)
+        self._free = _BlockFifo(self.num_blocks, order)
         self._rows = deque(range(self.max_seqs))
         # host tier: blocks of sequences moved out of the device pool
         self.num_host_blocks = int(num_host_blocks)
         self.host_ref = np.zeros(self.num_host_blocks, dtype=np.int32)
         self._host_free = deque(range(self.num_host_blocks))
         self.on_host = np.zeros(self.max_seqs, dtype=bool)
+        self._native_args = None                    # (free list, array pointers) of the native step
+        self._npairs = np.zeros(1, dtype=np.int32)
 
     # ---------------------------------------------------------------- blocks
     def _take(self, n: int) -> np.ndarray:
         """Hand out ``n`` blocks (the caller has checked ``_available``)."""
-        out = np.fromiter((self._free.popleft() for _ in range(n)), dtype=np.int32, count=n)
+        out = self._free.popleft_n(n)
         self.ref[out] = 1
         return out
 
@@ -92,7 +165,7 @@ class BlockAllocator:
 
     def _release(self, blocks) -> None:
         """Blocks whose count just reached zero, in logical order."""
-        self._free.extend(int(b) for b in blocks)
+        self._free.extend(blocks)
 
     def _idle(self):
         """Unreferenced blocks kept out of the free list (none here)."""
@@ -208,54 +281,34 @@ class BlockAllocator:
     def append_step(self, sids):
         """One new token for each sequence in ``sids`` (a decode step), handled
         in the order given.  Same result as ``append_tokens(s, 1)`` for each
-        ``s`` in turn, done with whole-batch array operations.
+        ``s`` in turn; the common case runs in the library's native step
+        (``block_manager_append_step``) on this object's arrays.
 
         Returns ``(slots int32[len(sids)], pairs int32[k][2])``.
         """
-        sids = np.asarray(sids, dtype=np.int64)
-        if len(np.unique(sids)) != len(sids):
-            raise ValueError("a sequence may appear once per step")
-        if not self.live[sids].all():
-            raise KeyError("append_step on a sequence that is not live")
-        if self.on_host[sids].any():
-            raise ValueError("append_step on a sequence on the host tier")
-        B = self.block_size
-        pos = self.lens[sids].astype(np.int64)
-        nb = self.nblk[sids].astype(np.int64)
-        need_new = pos % B == 0
-        last = np.where(need_new, 0, self.tables[sids, np.maximum(nb - 1, 0)]).astype(np.int64)
-        if self.sealed[last[~need_new]].any():
+        sids = np.ascontiguousarray(sids, dtype=np.int64)
+        n = len(sids)
+        slots = np.empty(n, dtype=np.int32)
+        pairs = np.empty((n, 2), dtype=np.int32)
+        if self._native_args is None or self._native_args[0] is not self._free:
+            self._native_args = (self._free, self._native_pointers())
+        rc = _native_step()(*self._native_args[1], sids.ctypes.data, n,
+                            self._free.ring.ctypes.data, self._free.state.ctypes.data,
+                            slots.ctypes.data, pairs.ctypes.data, self._npairs.ctypes.data)
+        if rc == 0:
+            return slots, pairs[:int(self._npairs[0])]
+        if rc in (_STEP_SEALED, _STEP_SHORT):
+            # a write into a sealed block (its copy may free it part-way), or
+            # more blocks than the free list holds (a subclass may evict)
             return self._append_step_in_turn(sids)
-        shared = (~need_new) & (self.ref[last] > 1)
-        cow = np.zeros(len(sids), dtype=bool)
-        ref_after = {}
-        for i in np.flatnonzero(shared):          # rare: seqs on a shared partial block
-            b = int(last[i])
-            c = ref_after.get(b, int(self.ref[b]))
-            if c > 1:
-                cow[i] = True
-                ref_after[b] = c - 1
-        takers = need_new | cow
-        k = int(takers.sum())
-        if k > self._available():
-            raise OutOfBlocks(f"need {k} blocks, {self._available()} free")
-        if (nb[need_new] + 1 > self.max_blocks_per_seq).any():
-            raise ValueError("sequence would exceed max_blocks_per_seq")
-        fresh = self._take(k)
-        idx = np.flatnonzero(takers)
-        got = np.empty(len(sids), dtype=np.int64)
-        got[idx] = fresh
-        for b, c in ref_after.items():
-            self.ref[b] = c
-        nn = np.flatnonzero(need_new)
-        self.tables[sids[nn], nb[nn]] = got[nn]
-        self.nblk[sids[nn]] += 1
-        cw = np.flatnonzero(cow)
-        self.tables[sids[cw], nb[cw] - 1] = got[cw]
-        pairs = np.stack([last[cw], got[cw]], axis=1).astype(np.int32)
-        slots = self.tables[sids, pos // B].astype(np.int64) * B + pos % B
-        self.lens[sids] += 1
-        return slots.astype(np.int32), pairs
+        msg = _native_error()
+        raise (KeyError if "not live" in msg else ValueError)(msg)
+
+    def _native_pointers(self):
+        return (self.tables.ctypes.data, self.lens.ctypes.data, self.nblk.ctypes.data,
+                self.live.ctypes.data, self.on_host.ctypes.data, self.max_seqs,
+                self.max_blocks_per_seq, self.ref.ctypes.data, self.sealed.ctypes.data,
+                self.num_blocks, self.block_size)
 
     def _append_step_in_turn(self, sids):
         """``append_tokens(s, 1)`` for each sequence in turn; used when a step
@@ -276,10 +329,11 @@ class BlockAllocator:
 
     def _snapshot(self):
         return (self.tables.copy(), self.lens.copy(), self.nblk.copy(), self.ref.copy(),
-                self.sealed.copy(), deque(self._free))
+                self.sealed.copy(), self._free.copy())
 
     def _restore(self, saved):
         self.tables, self.lens, self.nblk, self.ref, self.sealed, self._free = saved
+        self._native_args = None
 
     def fork(self, sid: int, n: int = 1):
         """``n`` new sequences sharing every block of ``sid`` by reference."""

@@ -133,6 +133,12 @@ int device_view(const void* p, void** out) {
 
 }  // namespace
 
+namespace pkv {
+// Error reporting for entry points defined in other files.
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+int clear_error() { return ok(); }
+}  // namespace pkv
+
 extern "C" {
 
 const char* paged_kv_last_error(void) { return g_err; }

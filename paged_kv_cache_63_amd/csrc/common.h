@@ -149,4 +149,9 @@ struct PrefixArgs {
 
 int launch_prefix(const PrefixArgs& a, hipStream_t st);
 
+// Set the per-thread message of paged_kv_last_error (entry points outside
+// the file that owns it); set_error returns code, clear_error PKV_OK.
+int set_error(int code, const char* msg);
+int clear_error();
+
 }  // namespace pkv

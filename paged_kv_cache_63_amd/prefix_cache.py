@@ -84,7 +84,7 @@ class PrefixCachingAllocator(BlockAllocator):
     def _take(self, n: int) -> np.ndarray:
         k = min(n, len(self._free))
         out = np.empty(n, dtype=np.int32)
-        out[:k] = [self._free.popleft() for _ in range(k)]
+        out[:k] = self._free.popleft_n(k)
         for i in range(k, n):                   # evict the least recently released
             b, _ = self._idle_lru.popitem(last=False)
             del self._block_of[self._digest.pop(b)]
@@ -95,7 +95,7 @@ class PrefixCachingAllocator(BlockAllocator):
 
     def _release(self, blocks) -> None:
         blocks = [int(b) for b in blocks]
-        self._free.extend(b for b in blocks if not self.sealed[b])
+        self._free.extend([b for b in blocks if not self.sealed[b]])
         for b in reversed(blocks):
             if self.sealed[b]:
                 self._idle_lru[b] = None
