@@ -210,7 +210,7 @@ def run_decode(args, case, torch, lib, alloc_cls):
         buf[:S] = sl
         buf[S:2 * S] = alloc.lens[:S]
         buf[2 * S:] = alloc.tables[:S].reshape(-1)
-        stage.copy_(ring[r], non_blocking=True)
+        lib.pinned_upload(stage, ring[r])      # index arrays, by a kernel on this stream
         ring_ev[r].record()
         if len(pairs):                                                       # a3
             lib.copy_blocks(k_pool, v_pool, torch.from_numpy(pairs).to(dev))
@@ -285,7 +285,7 @@ def run_extend(args, case, torch, lib, alloc_cls):
         buf = ring[r].numpy()
         buf[:n_new] = sl
         buf[n_new:] = alloc.tables[:R].reshape(-1)
-        stage.copy_(ring[r], non_blocking=True)
+        lib.pinned_upload(stage, ring[r])      # index arrays, by a kernel on this stream
         ring_ev[r].record()
         lib.paged_kv_append(k_new, v_new, slots_d, k_pool, v_pool)
         if timed:
@@ -356,6 +356,17 @@ def run_shared(args, case, torch, lib, alloc_cls):
     ev_pairs, snaps = [], []
     kv_per_tok = 2 * hkv * d * 2
     n_pairs = 0
+    # pinned staging per in-flight step: [slots | lens | tables], uploaded by a kernel
+    n_i32 = 2 * S + S * maxb
+    ring = [torch.empty(n_i32, dtype=torch.int32, pin_memory=True) for _ in range(3)]
+    ring_np = [r.numpy() for r in ring]
+    ring_ev = [torch.cuda.Event() for _ in range(3)]
+    for e in ring_ev:
+        e.record()
+    stage = torch.empty(n_i32, dtype=torch.int32, device=dev)
+    slots_d = stage[:S]
+    lens_d = stage[S:2 * S]
+    tables_d = stage[2 * S:].view(S, maxb)
     groups = None
     if not args.plain_decode:
         # the shared prompt's blocks lead every table for the whole run: the
@@ -373,10 +384,15 @@ def run_shared(args, case, torch, lib, alloc_cls):
         n_pairs += len(pairs)
         if len(pairs):
             lib.copy_blocks(k_pool, v_pool, torch.from_numpy(pairs).to(dev))
-        slots_d = torch.from_numpy(slots).to(dev, non_blocking=True)
         lens = alloc.lens[rows]
-        tables_d = torch.from_numpy(alloc.tables[rows]).to(dev, non_blocking=True)
-        lens_d = torch.from_numpy(lens).to(dev, non_blocking=True)
+        r = i % 3
+        ring_ev[r].synchronize()
+        buf = ring_np[r]
+        buf[:S] = slots
+        buf[S:2 * S] = lens
+        buf[2 * S:] = alloc.tables[rows].reshape(-1)
+        lib.pinned_upload(stage, ring[r])
+        ring_ev[r].record()
         lib.paged_kv_append(k_steps[i], v_steps[i], slots_d, k_pool, v_pool)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -325,6 +325,31 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_
                     int32_t block_size, int32_t dtype, void* stream);
 
 /*
+ * pinned_upload -- copy `bytes` bytes from src to dst with a kernel on
+ * `stream`, for the host block manager's per-step outputs (slot mapping,
+ * context lengths, block tables).  The pages put that bookkeeping beside the
+ * attention kernels, not in them ("Paged Attention for Efficient Memory
+ * Management", The Daily Triptych, technical summary: block tables and
+ * reference counts are the scheme's bookkeeping cost; "PagedAttention 与
+ * RadixAttention", section "RadixAttention": the tree lives in CPU memory),
+ * so its results cross to the device every step.  A kernel that reads the
+ * pinned buffer through its device mapping keeps that crossing on the
+ * compute queue, where a copy-engine transfer would add a hand-off between
+ * queues to every step.
+ *
+ *   dst    device memory (or pinned host memory), written
+ *   src    pinned host memory (hipHostMalloc, torch pin_memory) or device
+ *          memory; read by the kernel when it runs, so the caller keeps it
+ *          unchanged until the stream has passed the call
+ *   bytes  >= 0; 0 is a no-op.  Any alignment (16-byte pieces when both
+ *          pointers are 16-byte aligned).
+ *
+ * PKV_ERR_INVALID for a negative size, a null pointer, or memory that is
+ * neither device memory nor pinned host memory.  The ranges must not overlap.
+ */
+int pinned_upload(void* dst, const void* src, int64_t bytes, void* stream);
+
+/*
  * block_manager_append_step -- HOST call, the one exception to the device
  * conventions above: every pointer is host memory, nothing is enqueued and
  * no GPU is touched.  The decode step of the host block manager: one new

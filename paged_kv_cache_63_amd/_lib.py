@@ -22,7 +22,7 @@ PKV_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SYMBOLS = ("paged_kv_append", "copy_blocks", "swap_blocks", "paged_attention_decode_workspace_size",
            "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
            "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
-           "paged_kv_last_error", "block_manager_append_step")
+           "paged_kv_last_error", "block_manager_append_step", "pinned_upload")
 
 
 class PagedKVError(RuntimeError):
@@ -63,6 +63,8 @@ def load():
                                            i32, i32, i32, i32, f32, i32, p]
     lib.paged_kv_gather.restype = ctypes.c_int
     lib.paged_kv_gather.argtypes = [p, p, p, p, i32, p, i32, i32, i32, i32, i32, p]
+    lib.pinned_upload.restype = ctypes.c_int
+    lib.pinned_upload.argtypes = [p, p, ctypes.c_int64, p]
     lib.block_manager_append_step.restype = ctypes.c_int
     lib.block_manager_append_step.argtypes = [p, p, p, p, p, i32, i32, p, p, i32, i32, p, i32,
                                               p, p, p, p, p]
@@ -144,6 +146,23 @@ def copy_blocks(k_pool, v_pool, block_mapping):
         raise ValueError("block_mapping must be [N][2]")
     _check(load().copy_blocks(_ptr(k_pool), _ptr(v_pool), nb, _ptr(block_mapping),
                               block_mapping.shape[0], hkv, d, bs, dt, _stream()))
+
+
+def pinned_upload(dst, src, nbytes=None):
+    """Copy ``src`` (a pinned host tensor, or a device tensor) into the device
+    tensor ``dst`` with a kernel on the current stream; ``nbytes`` defaults to
+    ``src``'s size.  ``src`` must stay unchanged until the stream has passed
+    the copy (record an event after it)."""
+    if not dst.is_cuda:
+        raise ValueError("dst must be a device tensor")
+    if not (src.is_cuda or src.is_pinned()):
+        raise ValueError("src must be pinned host memory or a device tensor")
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("dst and src must be contiguous")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > dst.numel() * dst.element_size() or n > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds a buffer")
+    _check(load().pinned_upload(_ptr(dst), _ptr(src), n, _stream()))
 
 
 def new_host_pools(num_blocks, num_kv_heads, head_dim, block_size=16, dtype=torch.bfloat16):

@@ -198,6 +198,18 @@ int swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* sr
   return rc ? fail(rc, "swap_blocks launch failed") : ok();
 }
 
+int pinned_upload(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (bytes < 0) return fail(PKV_ERR_INVALID, "negative byte count");
+  if (bytes == 0) return ok();
+  if (!dst || !src) return fail(PKV_ERR_INVALID, "null pointer argument");
+  void* d = nullptr;
+  void* sv = nullptr;
+  if (device_view(dst, &d) || device_view(src, &sv))
+    return fail(PKV_ERR_INVALID, "buffers must be device memory or pinned host memory");
+  const int rc = pkv::launch_upload(d, sv, bytes, (hipStream_t)stream);
+  return rc ? fail(rc, "upload launch failed") : ok();
+}
+
 int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
                     int32_t num_blocks, const int32_t* block_table_row, int32_t context_len,
                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,

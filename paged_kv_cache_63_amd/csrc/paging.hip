@@ -246,6 +246,24 @@ __global__ __launch_bounds__(kThreads) void append_bulk_kernel(
   }
 }
 
+// Byte copy into device memory from a source the device can read (the
+// device mapping of pinned host memory): 16-byte pieces when both ends are
+// 16-byte aligned, then the remaining bytes one by one.
+__global__ __launch_bounds__(kThreads) void upload_kernel(uint8_t* __restrict__ dst,
+                                                          const uint8_t* __restrict__ src,
+                                                          int64_t bytes, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t done = 0;
+  if (vec) {
+    const int64_t n16 = bytes / 16;
+    for (int64_t i = t0; i < n16; i += stride)
+      reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
+    done = n16 * 16;
+  }
+  for (int64_t i = done + t0; i < bytes; i += stride) dst[i] = src[i];
+}
+
 // Block copy between two pools (one of them may be pinned host memory, seen
 // through its device mapping): every (pair, 16-byte piece) of the K and V
 // blocks, grid-stride; each thread has kSwapU pieces of K and of V in flight
@@ -407,6 +425,17 @@ int launch_gather(void* k_out, void* v_out, const void* k_pool, const void* v_po
     gather_kernel<4><<<grid, kThreads, 0, st>>>((uint8_t*)k_out, (uint8_t*)v_out,
                                                 (const uint8_t*)k_pool, (const uint8_t*)v_pool, row,
                                                 pieces, ppr, hkv, d, bs, num_blocks);
+  return status_of(hipGetLastError());
+}
+
+// The upload's grid: one round of 16-byte pieces for the sizes a step's
+// index arrays have, at most 1024 workgroups beyond that.
+int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st) {
+  const int vec = (((uintptr_t)dst | (uintptr_t)src) & 15) == 0;
+  const int64_t work = vec ? bytes / 16 + 16 : bytes;
+  int64_t g = (work + kThreads - 1) / kThreads;
+  g = g < 1 ? 1 : (g > 1024 ? 1024 : g);
+  upload_kernel<<<(unsigned)g, kThreads, 0, st>>>((uint8_t*)dst, (const uint8_t*)src, bytes, vec);
   return status_of(hipGetLastError());
 }
 

@@ -167,3 +167,29 @@ def test_decode_step_allocator_and_append(gpu):
         paging.append(kr, vr, kw, vw, np.asarray(want), 16)
     torch.cuda.synchronize()
     assert np.array_equal(words_of(k), kr) and np.array_equal(words_of(v), vr)
+
+
+@pytest.mark.parametrize("nbytes", [1, 15, 16, 17, 4099, 67840])
+@pytest.mark.parametrize("dst_off,src_off", [(0, 0), (4, 0), (0, 1), (3, 5)])
+def test_pinned_upload_bytes(gpu, nbytes, dst_off, src_off):
+    """Bytes from pinned host memory (and from device memory) land exactly;
+    the bytes around the destination range stay as they were."""
+    rng = np.random.default_rng(nbytes * 31 + dst_off * 7 + src_off)
+    payload = rng.integers(0, 256, nbytes + src_off, dtype=np.uint8)
+    src = torch.from_numpy(payload).pin_memory()[src_off:]
+    dst = torch.full((nbytes + dst_off + 8,), 0xA5, dtype=torch.uint8, device="cuda")
+    _lib.pinned_upload(dst[dst_off:dst_off + nbytes], src)
+    dev_src = torch.from_numpy(payload[src_off:].copy()).cuda()
+    dst2 = torch.full_like(dst, 0x5A)
+    _lib.pinned_upload(dst2[dst_off:dst_off + nbytes], dev_src)
+    torch.cuda.synchronize()
+    for d, fill in ((dst, 0xA5), (dst2, 0x5A)):
+        got = d.cpu().numpy()
+        assert np.array_equal(got[dst_off:dst_off + nbytes], payload[src_off:])
+        assert (got[:dst_off] == fill).all() and (got[dst_off + nbytes:] == fill).all()
+
+
+def test_pinned_upload_rejects_pageable_host_memory(gpu):
+    dst = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        _lib.pinned_upload(dst, torch.zeros(64, dtype=torch.uint8))
