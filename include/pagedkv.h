@@ -179,15 +179,24 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *                  and merged by the piece that finishes last.  fp32: fixed
  *                  partitions of partition_size tokens, then a merge pass.
  *   workspace      device memory of at least
- *                  paged_attention_decode_workspace_size(...) bytes, owned
- *                  by the caller, any contents (the call clears its
- *                  counters first).  Layout, P = ceil(max_context_len /
- *                  partition_size) + 1 pieces per context:
+ *                  paged_attention_decode_workspace_size(...) bytes, 8-byte
+ *                  aligned, owned by the caller, any contents (no clearing
+ *                  is needed between calls; see arrive below).  Layout,
+ *                  P = ceil(max_context_len / partition_size) + 1 pieces
+ *                  per context:
  *                    o_part [num_seqs][num_q_heads][P][head_dim]  fp32, a
  *                                                  piece's normalised output
  *                    m_part [num_seqs][num_q_heads][P]  fp32, max scaled score
  *                    l_part [num_seqs][num_q_heads][P]  fp32, sum exp(score - m)
- *                    counters [num_seqs][num_kv_heads]  int32, pieces arrived
+ *                    arrive [num_seqs][num_kv_heads]  uint64: bits 24..63
+ *                                  a per-call tag, bits 0..23 the pieces of
+ *                                  that call arrived.  A word with another
+ *                                  call's tag counts as no arrival, so old
+ *                                  contents are harmless; arbitrary contents
+ *                                  are misread only if a word holds exactly
+ *                                  the call's 40-bit tag (tags run in one
+ *                                  process-wide sequence from a random start
+ *                                  with the top bit set).
  *                  Piece k of a context is the k-th range it meets.  Calls
  *                  that share a workspace must not overlap in time.
  *                  Returns PKV_ERR_UNSUPPORTED (bf16) when one merge's

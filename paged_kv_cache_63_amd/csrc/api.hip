@@ -3,6 +3,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <random>
+
 #include "../../include/pagedkv.h"
 #include "common.h"
 
@@ -93,6 +96,20 @@ PrefixSplit prefix_split(int32_t num_groups, int32_t max_group_size, int32_t max
   int64_t blocks = (max_prefix_blocks + want - 1) / want;
   blocks = (blocks + 3) / 4 * 4;
   return {(int32_t)blocks, (int32_t)((max_prefix_blocks + blocks - 1) / blocks)};
+}
+
+// A tag per plain decode call for its arrival words (bits 24..63 of a word;
+// the count of the call's arrived pieces sits below).  Tags come from one
+// process-wide sequence that starts at a random point with its top bit set:
+// a word written by an earlier call carries an earlier tag, and a word the
+// library never wrote matches only if it happens to hold this exact tag.
+uint64_t next_call_tag() {
+  static std::atomic<uint64_t> next{[] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+  }()};
+  constexpr uint64_t kLow = (1ull << 39) - 1;
+  return ((1ull << 39) | (next.fetch_add(1, std::memory_order_relaxed) & kLow)) << 24;
 }
 
 // Byte offsets of the shared-prefix decode's workspace regions.
@@ -234,7 +251,7 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
   if (ptok <= 0) return 0;
   const int64_t P = max_pieces(max_context_len, ptok);
   return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float) +
-         (size_t)num_seqs * num_kv_heads * sizeof(int32_t);
+         (size_t)num_seqs * num_kv_heads * sizeof(uint64_t);
 }
 
 int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -271,6 +288,8 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
                                                             head_dim, max_context_len, ptok);
   if (!workspace || workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if ((uintptr_t)workspace % 8)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 8-byte aligned");
 
   pkv::DecodeArgs a{};
   a.out = out;
@@ -285,7 +304,9 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
     a.part_o = ws;
     a.part_m = ws + rows * head_dim;
     a.part_l = a.part_m + rows;
-    a.counters = (int32_t*)(a.part_l + rows);
+    // rows * (D + 2) floats: a multiple of 8 bytes, so the words are aligned
+    a.arrive = (uint64_t*)(a.part_l + rows);
+    a.tag = next_call_tag();
   }
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;

@@ -69,7 +69,12 @@ struct DecodeArgs {
   float* part_o;   // [S][Hq][P][D]
   float* part_m;   // [S][Hq][P]
   float* part_l;   // [S][Hq][P]
-  int32_t* counters;  // [S][Hkv] pieces arrived per unit (zero between calls)
+  int32_t* counters;  // shared-prefix decode: [S][Hkv] pieces per unit
+  // Plain decode: [S][Hkv] arrival words, bits 24..63 a call's tag and bits
+  // 0..23 the pieces of that call arrived so far; a word with another tag
+  // counts as zero, so the words need no clearing between calls.
+  uint64_t* arrive;
+  uint64_t tag;       // this call's tag, already in bits 24..63
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t num_seqs;

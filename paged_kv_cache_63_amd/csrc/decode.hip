@@ -410,9 +410,19 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid < n_pend) {
-    int32_t* arrivals = &a.counters[(int64_t)pend_s[tid] * hkv + pend_h[tid]];
-    const int prev = __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh_lastv[tid] = prev == pend_np[tid] - 1;
+    // count this piece in: a word that carries another call's tag holds
+    // no arrival of this call
+    uint64_t* w = &a.arrive[(int64_t)pend_s[tid] * hkv + pend_h[tid]];
+    constexpr uint64_t kCount = (1ull << 24) - 1;
+    uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t prev;
+    while (true) {
+      prev = (old & ~kCount) == a.tag ? (old & kCount) : 0;
+      if (__hip_atomic_compare_exchange_strong(w, &old, a.tag | (prev + 1), __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    sh_lastv[tid] = prev == (uint64_t)(pend_np[tid] - 1);
   }
   __syncthreads();
   for (int i = 0; i < n_pend; ++i)
@@ -581,8 +591,9 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 
-// Clears the arrival counters before the decode kernel counts into them
-// (a kernel rather than a memset, so the call can be captured in a graph).
+// Clears the shared-prefix decode's piece counts (and the per-sequence
+// prefix table beside them) before its kernels fill them (a kernel rather
+// than a memset, so the call can be captured in a graph).
 __global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* c, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) c[i] = 0;
 }
@@ -678,10 +689,8 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
       attr_set[a.seq_prefix != nullptr] = true;
     }
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
-    const int64_t cgrid = (units + 255) / 256;
-    if (!a.seq_prefix)   // the shared-prefix entry clears them with its own table
-      clear_counters_kernel<<<(int)(cgrid < 1024 ? (cgrid > 0 ? cgrid : 1) : 1024), 256, 0, st>>>(
-          a.counters, units);
+    // (plain decode: tagged arrival words, nothing to clear; the shared-prefix
+    // entry clears its piece counts with its own table)
     kern<<<a.num_workgroups, NW * kWave, lds, st>>>(a);
     if (a.seq_prefix) {
       hipError_t e = hipGetLastError();

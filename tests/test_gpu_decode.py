@@ -106,7 +106,8 @@ def decode_plan(lens, hkv, piece_tokens, workgroups):
 def test_partials_match_oracle_pieces(gpu):
     """Workspace after a call: each piece (o_p, m_p, l_p) of every split
     unit against the oracle's statistics over the same tokens, and each
-    unit's arrival count equal to its number of pieces."""
+    unit's arrival word holding the call's tag and a count equal to its
+    number of pieces."""
     case = decode_case(301, 3, 700, 1500, 16, 4, 128, "bf16")
     st = LibDecodeState(case)
     ptok = 64
@@ -121,7 +122,10 @@ def test_partials_match_oracle_pieces(gpu):
     o = w[:rows * d].reshape(S, hq, P, d)
     m = w[rows * d:rows * (d + 1)].reshape(S, hq, P)
     l = w[rows * (d + 1):rows * (d + 2)].reshape(S, hq, P)
-    counters = raw[rows * (d + 2) * 4:rows * (d + 2) * 4 + S * hkv * 4].view(np.int32)
+    words = raw[rows * (d + 2) * 4:rows * (d + 2) * 4 + S * hkv * 8].view(np.uint64)
+    counters = (words & np.uint64((1 << 24) - 1)).astype(np.int64)
+    tags = words >> np.uint64(24)
+    assert (tags == tags[0]).all() and int(tags[0]) >> 39 == 1     # one call's tag, top bit set
     expect = np.zeros(S * hkv, np.int64)
     wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     checked = 0
@@ -195,16 +199,22 @@ def test_context_longer_than_declared_max_is_cut_not_overrun(gpu):
     assert np.abs(f64_of(out) - want).max() <= 2e-2
 
 
-def test_workspace_reused_across_calls(gpu):
+@pytest.mark.parametrize("fill", ["5a", "ff", "00", "random"])
+def test_workspace_reused_across_calls(gpu, fill):
     """One workspace (filled with garbage first) serves consecutive calls of
-    different shapes, whose counters and pieces sit at different offsets:
-    every output matches the oracle."""
+    different shapes, whose arrival words and pieces sit at different
+    offsets: the words need no clearing, and every output matches the
+    oracle."""
     cases = [decode_case(811, 5, 200, 2500, 32, 8, 128, "bf16"),
              decode_case(812, 9, 1, 900, 32, 8, 128, "bf16"),
              decode_case(813, 2, 1500, 3000, 32, 8, 128, "bf16")]
     need = max(_lib.paged_attention_decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads,
                                                           c.head_dim, 3000, 64) for c in cases)
-    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    if fill == "random":
+        g = torch.Generator().manual_seed(5)
+        ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=g).cuda()
+    else:
+        ws = torch.full((need,), int(fill, 16), dtype=torch.uint8, device="cuda")
     for rep in range(2):
         for c in cases:
             st = LibDecodeState(c)

@@ -51,14 +51,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_workspace_size_formula(lib):
     """pieces P = ceil(max_context_len / piece) + 1 per (sequence, query
-    head), each (o[D], m, l) in fp32, then one int32 arrival counter per
+    head), each (o[D], m, l) in fp32, then one uint64 arrival word per
     (sequence, KV head); the piece is 512 tokens unless given."""
     ws = lib.paged_attention_decode_workspace_size
-    assert ws(64, 32, 8, 128, 4096, 512) == 64 * 32 * 9 * 130 * 4 + 64 * 8 * 4
-    assert ws(64, 32, 8, 128, 512, 512) == 64 * 32 * 2 * 130 * 4 + 64 * 8 * 4
-    assert ws(8, 64, 8, 128, 131072, 0) == 8 * 64 * 257 * 130 * 4 + 8 * 8 * 4
-    assert ws(1, 8, 1, 128, 8192, 0) == 1 * 8 * 17 * 130 * 4 + 1 * 1 * 4
-    assert ws(1, 8, 1, 64, 0, 64) == 1 * 8 * 1 * 66 * 4 + 4
+    assert ws(64, 32, 8, 128, 4096, 512) == 64 * 32 * 9 * 130 * 4 + 64 * 8 * 8
+    assert ws(64, 32, 8, 128, 512, 512) == 64 * 32 * 2 * 130 * 4 + 64 * 8 * 8
+    assert ws(8, 64, 8, 128, 131072, 0) == 8 * 64 * 257 * 130 * 4 + 8 * 8 * 8
+    assert ws(1, 8, 1, 128, 8192, 0) == 1 * 8 * 17 * 130 * 4 + 1 * 1 * 8
+    assert ws(1, 8, 1, 64, 0, 64) == 1 * 8 * 1 * 66 * 4 + 8
     assert ws(0, 8, 1, 64, 100, 64) == 0
 
 
@@ -87,6 +87,11 @@ def test_bad_arguments_rejected(lib):
     rc = lib.paged_attention_decode(one, one, one, one, 10, one, 4, one, 2, 4096, 32, 8, 128, 16,
                                     ctypes.c_float(0.1), 512, null, 0, 1, None)
     assert rc == -3
+    # misaligned workspace
+    rc = lib.paged_attention_decode(one, one, one, one, 10, one, 4, one, 2, 4096, 32, 8, 128, 16,
+                                    ctypes.c_float(0.1), 512, ctypes.c_void_p(4100), 1 << 30, 1,
+                                    None)
+    assert rc == -3 and b"aligned" in lib.paged_kv_last_error()
     # partition size not a block multiple
     rc = lib.paged_attention_decode(one, one, one, one, 10, one, 4, one, 2, 4096, 32, 8, 128, 16,
                                     ctypes.c_float(0.1), 100, null, 0, 1, None)
