@@ -149,7 +149,7 @@ class BlockAllocator:
         self.host_ref = np.zeros(self.num_host_blocks, dtype=np.int32)
         self._host_free = deque(range(self.num_host_blocks))
         self.on_host = np.zeros(self.max_seqs, dtype=bool)
-        self._native_args = None                    # (free list, array pointers) of the native step
+        self._native_args = None                    # (state arrays, their pointers) for the native step
         self._npairs = np.zeros(1, dtype=np.int32)
 
     # ---------------------------------------------------------------- blocks
@@ -290,9 +290,12 @@ class BlockAllocator:
         n = len(sids)
         slots = np.empty(n, dtype=np.int32)
         pairs = np.empty((n, 2), dtype=np.int32)
-        if self._native_args is None or self._native_args[0] is not self._free:
-            self._native_args = (self._free, self._native_pointers())
-        rc = _native_step()(*self._native_args[1], sids.ctypes.data, n,
+        arrays = (self.tables, self.lens, self.nblk, self.live, self.on_host, self.ref,
+                  self.sealed, self._free)
+        cached = self._native_args
+        if cached is None or any(x is not y for x, y in zip(cached[0], arrays)):
+            self._native_args = cached = (arrays, self._native_pointers())
+        rc = _native_step()(*cached[1], sids.ctypes.data, n,
                             self._free.ring.ctypes.data, self._free.state.ctypes.data,
                             slots.ctypes.data, pairs.ctypes.data, self._npairs.ctypes.data)
         if rc == 0:
