@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=WORKLOADS, default="gqa4-decode")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="decode workloads: time the decode call with HIP events on every n-th "
+                         "timed step (1 = every step)")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--plain-decode", action="store_true",
                     help="shared-prefix workload: decode every sequence on its own "
@@ -193,7 +196,6 @@ def run_decode(args, case, torch, lib, alloc_cls):
     for e in ring_ev:
         e.record()
     stage = torch.empty(n_i32, dtype=torch.int32, device=dev)
-    slots_d = stage[:S]
     lens_d = stage[S:2 * S]
     tables_d = stage[2 * S:].view(S, maxb)
     torch.cuda.synchronize()
@@ -210,18 +212,21 @@ def run_decode(args, case, torch, lib, alloc_cls):
         buf[:S] = sl
         buf[S:2 * S] = alloc.lens[:S]
         buf[2 * S:] = alloc.tables[:S].reshape(-1)
-        lib.pinned_upload(stage, ring[r])      # index arrays, by a kernel on this stream
-        ring_ev[r].record()
         if len(pairs):                                                       # a3
             lib.copy_blocks(k_pool, v_pool, torch.from_numpy(pairs).to(dev))
-        lib.paged_kv_append(k_steps[i], v_steps[i], slots_d, k_pool, v_pool)  # a2
+        # a2, with the step's index arrays going up in the same launch
+        lib.upload_and_append(stage, ring[r], k_steps[i], v_steps[i], k_pool, v_pool)
+        ring_ev[r].record()
         mcl = int(alloc.lens[:S].max())
-        if timed:
+        # the decode call is bracketed by timing events on every event_every-th
+        # timed step (each event is a marker the GPU processes between kernels)
+        sample = timed and (i - args.warmup) % args.event_every == 0
+        if sample:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
         lib.paged_attention_decode(out, q_steps[i], k_pool, v_pool, tables_d, lens_d, mcl,
                                    case.scale, args.partition_size, ws)       # a4 + a5
-        if timed:
+        if sample:
             e1.record()
             ev_pairs.append((e0, e1))
             lens_seen.append(alloc.lens[:S].copy())     # bytes are counted after timing
@@ -271,7 +276,7 @@ def run_extend(args, case, torch, lib, alloc_cls):
     for e in ring_ev:
         e.record()
     stage = torch.empty(n_new + R * maxb, dtype=torch.int32, device=dev)
-    slots_d, tables_d = stage[:n_new], stage[n_new:].view(R, maxb)
+    tables_d = stage[n_new:].view(R, maxb)
     T = args.warmup + args.steps
     flops = 4.0 * d * hq * float(sum(int(n) * int(p) + int(n) * (int(n) + 1) / 2
                                      for p, n in zip(case.prefix_lens, case.new_lens)))
@@ -285,9 +290,8 @@ def run_extend(args, case, torch, lib, alloc_cls):
         buf = ring[r].numpy()
         buf[:n_new] = sl
         buf[n_new:] = alloc.tables[:R].reshape(-1)
-        lib.pinned_upload(stage, ring[r])      # index arrays, by a kernel on this stream
+        lib.upload_and_append(stage, ring[r], k_new, v_new, k_pool, v_pool)   # index arrays + a2
         ring_ev[r].record()
-        lib.paged_kv_append(k_new, v_new, slots_d, k_pool, v_pool)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -364,7 +368,6 @@ def run_shared(args, case, torch, lib, alloc_cls):
     for e in ring_ev:
         e.record()
     stage = torch.empty(n_i32, dtype=torch.int32, device=dev)
-    slots_d = stage[:S]
     lens_d = stage[S:2 * S]
     tables_d = stage[2 * S:].view(S, maxb)
     groups = None
@@ -391,9 +394,8 @@ def run_shared(args, case, torch, lib, alloc_cls):
         buf[:S] = slots
         buf[S:2 * S] = lens
         buf[2 * S:] = alloc.tables[rows].reshape(-1)
-        lib.pinned_upload(stage, ring[r])
+        lib.upload_and_append(stage, ring[r], k_steps[i], v_steps[i], k_pool, v_pool)
         ring_ev[r].record()
-        lib.paged_kv_append(k_steps[i], v_steps[i], slots_d, k_pool, v_pool)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -608,6 +610,8 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         sys.exit("--steps must be >= 1 and --warmup >= 0")
 
+    if args.event_every < 1:
+        sys.exit("--event-every must be at least 1")
     if args.workload == "prefix-cache-host":     # host-side only: no GPU involved
         run_prefix_host(args)
         return

@@ -359,6 +359,35 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_
 int pinned_upload(void* dst, const void* src, int64_t bytes, void* stream);
 
 /*
+ * upload_and_append -- pinned_upload and paged_kv_append in one call, for a
+ * decode step whose staging buffer carries the slot mapping among its index
+ * arrays.  The kernel copies `bytes` bytes of `staging` to `dst` and, at the
+ * same time, writes the new tokens' keys and values into their slots
+ * ("Paged Attention for Efficient Memory Management", The Daily Triptych,
+ * "The story": a new token's keys and values go into the next slot of its
+ * sequence's block), reading each token's slot from `staging` itself, so
+ * the two parts do not wait for each other.  From 512 tokens on it runs as
+ * the upload followed by paged_kv_append's bulk path (which reads the slots
+ * from the device copy), i.e. two launches.
+ *
+ *   dst, staging, bytes   as pinned_upload (bytes >= 0; 0 is a no-op)
+ *   slots_offset          byte offset of the slot mapping, int32
+ *                         [num_tokens], inside staging: a multiple of 4,
+ *                         slots_offset + 4 * num_tokens <= bytes
+ *   k_new, v_new, num_tokens, k_pool, v_pool, num_blocks, num_kv_heads,
+ *   head_dim, block_size, dtype   as paged_kv_append
+ *
+ * The pool writes happen after every earlier call on `stream` (a
+ * copy_blocks for the step's copy-on-write pairs goes first).  Errors as
+ * pinned_upload and paged_kv_append, plus PKV_ERR_INVALID for a slot
+ * mapping outside the staged bytes.
+ */
+int upload_and_append(void* dst, const void* staging, int64_t bytes, int64_t slots_offset,
+                      const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
+                      void* v_pool, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t dtype, void* stream);
+
+/*
  * block_manager_append_step -- HOST call, the one exception to the device
  * conventions above: every pointer is host memory, nothing is enqueued and
  * no GPU is touched.  The decode step of the host block manager: one new

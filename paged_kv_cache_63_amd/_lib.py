@@ -22,7 +22,8 @@ PKV_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 SYMBOLS = ("paged_kv_append", "copy_blocks", "swap_blocks", "paged_attention_decode_workspace_size",
            "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
            "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
-           "paged_kv_last_error", "block_manager_append_step", "pinned_upload")
+           "paged_kv_last_error", "block_manager_append_step", "pinned_upload",
+           "upload_and_append")
 
 
 class PagedKVError(RuntimeError):
@@ -65,6 +66,9 @@ def load():
     lib.paged_kv_gather.argtypes = [p, p, p, p, i32, p, i32, i32, i32, i32, i32, p]
     lib.pinned_upload.restype = ctypes.c_int
     lib.pinned_upload.argtypes = [p, p, ctypes.c_int64, p]
+    lib.upload_and_append.restype = ctypes.c_int
+    lib.upload_and_append.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, p, p, i32, p, p, i32,
+                                      i32, i32, i32, i32, p]
     lib.block_manager_append_step.restype = ctypes.c_int
     lib.block_manager_append_step.argtypes = [p, p, p, p, p, i32, i32, p, p, i32, i32, p, i32,
                                               p, p, p, p, p]
@@ -163,6 +167,29 @@ def pinned_upload(dst, src, nbytes=None):
     if n > dst.numel() * dst.element_size() or n > src.numel() * src.element_size():
         raise ValueError("nbytes exceeds a buffer")
     _check(load().pinned_upload(_ptr(dst), _ptr(src), n, _stream()))
+
+
+def upload_and_append(dst, staging, k_new, v_new, k_pool, v_pool, slots_at=0):
+    """:func:`pinned_upload` of the int32 ``staging`` buffer into ``dst`` and
+    :func:`paged_kv_append` of ``k_new``/``v_new`` whose slot mapping is
+    ``staging[slots_at : slots_at + len(k_new)]``, in one call."""
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    _dev(k_new, v_new, k_pool, v_pool)
+    if not dst.is_cuda or not (staging.is_cuda or staging.is_pinned()):
+        raise ValueError("dst must be a device tensor and staging pinned (or on the device)")
+    if staging.dtype != torch.int32 or not (dst.is_contiguous() and staging.is_contiguous()):
+        raise ValueError("staging must be a contiguous int32 tensor, dst contiguous")
+    T = k_new.shape[0]
+    if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d):
+        raise ValueError("k_new/v_new must be [T][Hkv][D]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new/v_new dtype must match the pools")
+    n = staging.numel() * 4
+    if n > dst.numel() * dst.element_size():
+        raise ValueError("dst is smaller than staging")
+    _check(load().upload_and_append(_ptr(dst), _ptr(staging), n, 4 * int(slots_at), _ptr(k_new),
+                                    _ptr(v_new), T, _ptr(k_pool), _ptr(v_pool), nb, hkv, d, bs,
+                                    dt, _stream()))
 
 
 def new_host_pools(num_blocks, num_kv_heads, head_dim, block_size=16, dtype=torch.bfloat16):

@@ -50,6 +50,10 @@ int launch_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, const int
                        int32_t num_pairs, int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
                        hipStream_t st);
 int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st);
+int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slots_offset,
+                         const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
+                         void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d,
+                         int32_t elem_bytes, hipStream_t st);
 int launch_swap_blocks(void* dst_k, void* dst_v, int32_t num_dst, const void* src_k,
                        const void* src_v, int32_t num_src, const int32_t* mapping,
                        int32_t num_pairs, int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,

@@ -17,16 +17,16 @@ constexpr int kBulkTokens = 512;  // appends of at least this many tokens look f
 // The key piece is stored as it is (rows are contiguous in the K pool); the
 // value piece is split into its 16/E elements, each going to its channel's
 // row of the transposed V block.
+// (Workgroup wg of nwg doing this work.)
 template <int E>
-__global__ __launch_bounds__(kThreads) void append_kernel(
+__device__ __forceinline__ void append_pieces(
     const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
     const int32_t* __restrict__ slots, int64_t pieces, int32_t pieces_per_row, int32_t hkv,
     int32_t d, int32_t bs, int32_t num_blocks, uint8_t* __restrict__ k_pool,
-    uint8_t* __restrict__ v_pool) {
+    uint8_t* __restrict__ v_pool, int64_t wg, int64_t nwg) {
   constexpr int kPer = 16 / E;  // elements per piece
   const int64_t row_bytes = (int64_t)d * E;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < pieces;
-       i += (int64_t)gridDim.x * kThreads) {
+  for (int64_t i = wg * kThreads + threadIdx.x; i < pieces; i += nwg * kThreads) {
     const int64_t row = i / pieces_per_row;        // token * hkv + head
     const int32_t piece = (int32_t)(i - row * pieces_per_row);
     const int64_t t = row / hkv;
@@ -54,6 +54,16 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
       for (int e = 0; e < kPer; ++e) *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * bs * E) = w[e];
     }
   }
+}
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void append_kernel(
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, int64_t pieces, int32_t pieces_per_row, int32_t hkv,
+    int32_t d, int32_t bs, int32_t num_blocks, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool) {
+  append_pieces<E>(k_new, v_new, slots, pieces, pieces_per_row, hkv, d, bs, num_blocks, k_pool,
+                   v_pool, blockIdx.x, gridDim.x);
 }
 
 // grid.y = pair; each thread copies 16-byte pieces of the K block and of the
@@ -249,11 +259,11 @@ __global__ __launch_bounds__(kThreads) void append_bulk_kernel(
 // Byte copy into device memory from a source the device can read (the
 // device mapping of pinned host memory): 16-byte pieces when both ends are
 // 16-byte aligned, then the remaining bytes one by one.
-__global__ __launch_bounds__(kThreads) void upload_kernel(uint8_t* __restrict__ dst,
-                                                          const uint8_t* __restrict__ src,
-                                                          int64_t bytes, int vec) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+__device__ __forceinline__ void upload_bytes(uint8_t* __restrict__ dst,
+                                             const uint8_t* __restrict__ src, int64_t bytes,
+                                             int vec, int64_t wg, int64_t nwg) {
+  const int64_t stride = nwg * kThreads;
+  const int64_t t0 = wg * kThreads + threadIdx.x;
   int64_t done = 0;
   if (vec) {
     const int64_t n16 = bytes / 16;
@@ -262,6 +272,30 @@ __global__ __launch_bounds__(kThreads) void upload_kernel(uint8_t* __restrict__ 
     done = n16 * 16;
   }
   for (int64_t i = done + t0; i < bytes; i += stride) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(kThreads) void upload_kernel(uint8_t* __restrict__ dst,
+                                                          const uint8_t* __restrict__ src,
+                                                          int64_t bytes, int vec) {
+  upload_bytes(dst, src, bytes, vec, blockIdx.x, gridDim.x);
+}
+
+// A decode step's host->device traffic in one launch: workgroups
+// [0, up_wgs) copy the staging buffer as upload_kernel does, the others
+// write the new tokens as append_kernel does, reading each token's slot
+// from the staging buffer itself (through its device mapping), so neither
+// part waits for the other.
+template <int E>
+__global__ __launch_bounds__(kThreads) void upload_append_kernel(
+    uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int64_t bytes, int vec,
+    int32_t up_wgs, const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, int64_t pieces, int32_t pieces_per_row, int32_t hkv,
+    int32_t d, int32_t num_blocks, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool) {
+  if ((int32_t)blockIdx.x < up_wgs)
+    upload_bytes(dst, src, bytes, vec, blockIdx.x, up_wgs);
+  else
+    append_pieces<E>(k_new, v_new, slots, pieces, pieces_per_row, hkv, d, 16, num_blocks, k_pool,
+                     v_pool, blockIdx.x - up_wgs, gridDim.x - up_wgs);
 }
 
 // Block copy between two pools (one of them may be pinned host memory, seen
@@ -430,12 +464,51 @@ int launch_gather(void* k_out, void* v_out, const void* k_pool, const void* v_po
 
 // The upload's grid: one round of 16-byte pieces for the sizes a step's
 // index arrays have, at most 1024 workgroups beyond that.
-int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st) {
-  const int vec = (((uintptr_t)dst | (uintptr_t)src) & 15) == 0;
+static int upload_vec(const void* dst, const void* src) {
+  return (((uintptr_t)dst | (uintptr_t)src) & 15) == 0;
+}
+
+static int64_t upload_grid(int64_t bytes, int vec) {
   const int64_t work = vec ? bytes / 16 + 16 : bytes;
-  int64_t g = (work + kThreads - 1) / kThreads;
-  g = g < 1 ? 1 : (g > 1024 ? 1024 : g);
-  upload_kernel<<<(unsigned)g, kThreads, 0, st>>>((uint8_t*)dst, (const uint8_t*)src, bytes, vec);
+  const int64_t g = (work + kThreads - 1) / kThreads;
+  return g < 1 ? 1 : (g > 1024 ? 1024 : g);
+}
+
+int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st) {
+  const int vec = upload_vec(dst, src);
+  upload_kernel<<<(unsigned)upload_grid(bytes, vec), kThreads, 0, st>>>(
+      (uint8_t*)dst, (const uint8_t*)src, bytes, vec);
+  return status_of(hipGetLastError());
+}
+
+int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slots_offset,
+                         const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
+                         void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d,
+                         int32_t elem_bytes, hipStream_t st) {
+  if (num_tokens == 0) return bytes > 0 ? launch_upload(dst, src, bytes, st) : 0;
+  if (num_tokens >= kBulkTokens) {
+    // bulk: the window scans read the slots many times, from the device copy
+    int rc = bytes > 0 ? launch_upload(dst, src, bytes, st) : 0;
+    if (rc) return rc;
+    return launch_append(k_new, v_new, (const int32_t*)((const uint8_t*)dst + slots_offset),
+                         num_tokens, k_pool, v_pool, num_blocks, hkv, d, 16, elem_bytes, st);
+  }
+  const int vec = upload_vec(dst, src);
+  const int64_t up = upload_grid(bytes, vec);
+  const int32_t ppr = d * elem_bytes / 16;
+  const int64_t pieces = (int64_t)num_tokens * hkv * ppr;
+  const int64_t g = up + grid_for(pieces);
+  const int32_t* slots = (const int32_t*)((const uint8_t*)src + slots_offset);
+  if (elem_bytes == 2)
+    upload_append_kernel<2><<<(unsigned)g, kThreads, 0, st>>>(
+        (uint8_t*)dst, (const uint8_t*)src, bytes, vec, (int32_t)up, (const uint8_t*)k_new,
+        (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, num_blocks, (uint8_t*)k_pool,
+        (uint8_t*)v_pool);
+  else
+    upload_append_kernel<4><<<(unsigned)g, kThreads, 0, st>>>(
+        (uint8_t*)dst, (const uint8_t*)src, bytes, vec, (int32_t)up, (const uint8_t*)k_new,
+        (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, num_blocks, (uint8_t*)k_pool,
+        (uint8_t*)v_pool);
   return status_of(hipGetLastError());
 }
 

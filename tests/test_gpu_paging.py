@@ -193,3 +193,39 @@ def test_pinned_upload_rejects_pageable_host_memory(gpu):
     dst = torch.empty(64, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError):
         _lib.pinned_upload(dst, torch.zeros(64, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("n", [0, 64, 300, 600])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_upload_and_append_matches_separate_calls(gpu, n, dtype, d):
+    """One call = pinned_upload of the staging buffer + paged_kv_append with
+    the slot mapping found inside it (at an offset), bit for bit: below 512
+    tokens in one launch, from 512 on as upload + bulk append."""
+    hkv, nb = 4, 96
+    rng = np.random.default_rng(n * 3 + d)
+    slots = rng.permutation(nb * 16)[:n].astype(np.int32)
+    if n:
+        slots[rng.integers(0, n, max(1, n // 20))] = -1          # skipped tokens
+    head = rng.integers(0, 1000, 37).astype(np.int32)              # other index arrays
+    tail = rng.integers(-5, 1000, 101).astype(np.int32)
+    staging = torch.from_numpy(np.concatenate([head, slots, tail])).pin_memory()
+    kw = normal_words(rng, (n, hkv, d), dtype)
+    vw = normal_words(rng, (n, hkv, d), dtype)
+    kn, vn = to_dev(kw, dtype), to_dev(vw, dtype)
+    k1, v1 = poisoned_pools(nb, hkv, d, dtype)
+    k2, v2 = poisoned_pools(nb, hkv, d, dtype)
+    dst1 = torch.full((staging.numel() + 3,), -7, dtype=torch.int32, device="cuda")
+    dst2 = torch.full_like(dst1, -7)
+    _lib.upload_and_append(dst1[:staging.numel()], staging, kn, vn, k1, v1, slots_at=len(head))
+    _lib.pinned_upload(dst2[:staging.numel()], staging)
+    if n:
+        _lib.paged_kv_append(kn, vn, dst2[len(head):len(head) + n], k2, v2)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst1.cpu().numpy(), dst2.cpu().numpy())
+    assert (dst1.cpu().numpy()[staging.numel():] == -7).all()
+    assert np.array_equal(words_of(k1), words_of(k2))
+    assert np.array_equal(words_of(v1), words_of(v2))
+    k0, v0 = poisoned_pools(nb, hkv, d, dtype)                     # and against the oracle
+    kp, vp = words_of(k0).copy(), words_of(v0).copy()
+    paging.append(kp, vp, kw, vw, slots, 16)
+    assert np.array_equal(words_of(k1), kp) and np.array_equal(words_of(v1), vp)

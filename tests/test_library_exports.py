@@ -96,6 +96,11 @@ def test_bad_arguments_rejected(lib):
     rc = lib.paged_attention_decode(one, one, one, one, 10, one, 4, one, 2, 4096, 32, 8, 128, 16,
                                     ctypes.c_float(0.1), 100, null, 0, 1, None)
     assert rc == -1
+    # upload + append: slot mapping misaligned or past the staged bytes
+    assert lib.upload_and_append(one, one, 64, 2, one, one, 4, one, one, 10, 8, 128, 16, 1,
+                                 None) == -1
+    assert lib.upload_and_append(one, one, 64, 60, one, one, 4, one, one, 10, 8, 128, 16, 1,
+                                 None) == -1 and b"staged" in lib.paged_kv_last_error()
     # upload: negative size, null pointer
     assert lib.pinned_upload(one, one, -1, None) == -1
     assert lib.pinned_upload(null, one, 16, None) == -1 and b"null" in lib.paged_kv_last_error()
@@ -106,6 +111,8 @@ def test_empty_calls_are_no_ops(lib):
     assert lib.paged_kv_append(null, null, null, 0, null, null, 10, 8, 128, 16, 1, None) == 0
     assert lib.copy_blocks(null, null, 10, null, 0, 8, 128, 16, 1, None) == 0
     assert lib.pinned_upload(null, null, 0, None) == 0
+    assert lib.upload_and_append(null, null, 0, 0, null, null, 0, null, null, 10, 8, 128, 16, 1,
+                                 None) == 0
     assert lib.paged_kv_last_error() == b""
 
 
