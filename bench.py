@@ -605,7 +605,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "this build has no multi-GPU path", file=sys.stderr)
+              "the paged-attention path here runs on a single GPU", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         sys.exit("--steps must be >= 1 and --warmup >= 0")
