@@ -243,8 +243,13 @@ def run_decode(args, case, torch, lib, alloc_cls):
     step_bytes = [int(ln.sum()) * kv_per_tok + 2 * S * hq * d * 2 + int((-(-ln // 16)).sum()) * 4
                   + S * 4 for ln in lens_seen]
     alloc.validate()
-    return dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=step_bytes,
-                ctx_mean=float(alloc.lens[:S].mean()))
+    res = dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=step_bytes,
+               ctx_mean=float(alloc.lens[:S].mean()))
+    if getattr(args, "keep_state", False):     # for tests of this loop: what the last step saw
+        res["state"] = dict(out=out, q=q_steps[T - 1], k_new=k_steps[T - 1], v_new=v_steps[T - 1],
+                            k_pool=k_pool, v_pool=v_pool, tables=alloc.tables[:S].copy(),
+                            lens=alloc.lens[:S].copy())
+    return res
 
 
 def run_extend(args, case, torch, lib, alloc_cls):

@@ -1,0 +1,46 @@
+"""The decode loop that bench.py times computes what the oracle computes.
+
+After a few timed steps of the GQA-4 workload at full size (64 sequences,
+~150K context tokens), through the same function the benchmark times (host
+allocator step, upload of the index arrays fused with the append, decode):
+the last step's output rows for sampled sequences match the oracle's decode
+over the pool the loop left behind, and the last step's new keys and values
+sit in their slots bit for bit.  Tolerance as for every bf16 decode: 2e-2
+max-abs."""
+
+import argparse
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from gpu_helpers import f64_of, words_of
+from oracle import attention, paging
+from paged_kv_cache_63_amd import BlockAllocator, _lib
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_loop_output_and_appends(gpu):
+    args = argparse.Namespace(warmup=2, steps=3, partition_size=0, event_every=1,
+                              keep_state=True)
+    case = bench.make_case("gqa4-decode", args.warmup + args.steps)
+    r = bench.run_decode(args, case, torch, _lib, BlockAllocator)
+    st = r["state"]
+    torch.cuda.synchronize()
+    assert len(r["durs"]) == args.steps and all(d > 0 for d in r["durs"])
+    kp, vp = words_of(st["k_pool"]), words_of(st["v_pool"])
+    lens = st["lens"]
+    tables = [row[:-(-int(L) // 16)].tolist() for row, L in zip(st["tables"], lens)]
+    seqs = [0, 17, 40, 63]
+    want = attention.decode(words_of(st["q"]), kp, vp, tables, lens, case.scale, 16, "bf16",
+                            seqs=seqs)
+    got = f64_of(st["out"])
+    assert np.abs(got[seqs] - want[seqs]).max() <= 2e-2
+    kn, vn = words_of(st["k_new"]), words_of(st["v_new"])
+    for s in range(case.num_seqs):
+        p = int(lens[s]) - 1                      # the last step's token
+        blk, off = tables[s][p // 16], p % 16
+        assert np.array_equal(kp[blk, :, off, :], kn[s])
+        assert np.array_equal(vp[blk, :, :, paging.v_pos(off)], vn[s])
