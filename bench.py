@@ -317,7 +317,11 @@ def run_extend(args, case, torch, lib, alloc_cls):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
-    return dict(elapsed=el, tokens=n_new * args.steps, durs=durs, flops=flops)
+    res = dict(elapsed=el, tokens=n_new * args.steps, durs=durs, flops=flops)
+    if getattr(args, "keep_state", False):     # for tests of this loop: what the last step saw
+        res["state"] = dict(out=out, k_pool=k_pool, v_pool=v_pool,
+                            tables=tables_d.cpu().numpy().copy())
+    return res
 
 
 def run_shared(args, case, torch, lib, alloc_cls):

@@ -1,4 +1,4 @@
-"""The decode loop that bench.py times computes what the oracle computes.
+"""The loops that bench.py times compute what the oracle computes.
 
 After a few timed steps of the GQA-4 workload at full size (64 sequences,
 ~150K context tokens), through the same function the benchmark times (host
@@ -44,3 +44,23 @@ def test_decode_loop_output_and_appends(gpu):
         blk, off = tables[s][p // 16], p % 16
         assert np.array_equal(kp[blk, :, off, :], kn[s])
         assert np.array_equal(vp[blk, :, :, paging.v_pos(off)], vn[s])
+
+
+def test_extend_loop_output(gpu):
+    """The multi-turn extend loop (16 requests, 2K-8K cached tokens + 512 new
+    each): the last step's output for 2 requests x 2 query heads against the
+    oracle over the pool and tables that step used."""
+    args = argparse.Namespace(warmup=1, steps=2, keep_state=True)
+    e = bench.make_case("multiturn-extend", args.warmup + args.steps)
+    r = bench.run_extend(args, e, torch, _lib, BlockAllocator)
+    st = r["state"]
+    torch.cuda.synchronize()
+    kp, vp = words_of(st["k_pool"]), words_of(st["v_pool"])
+    tables = [row[:-(-int(L) // 16)].tolist() for row, L in zip(st["tables"], e.seq_lens)]
+    reqs, heads = [int(np.argmax(e.prefix_lens)), 3], [0, 29]
+    want = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tables, e.scale, 16, "bf16",
+                            reqs=reqs, heads=heads)
+    got = f64_of(st["out"])
+    for q in reqs:
+        a, b = int(e.cu_new[q]), int(e.cu_new[q + 1])
+        assert np.abs(got[a:b][:, heads] - want[a:b][:, heads]).max() <= 2e-2, q
