@@ -186,7 +186,7 @@ def run_decode(args, case, torch, lib, alloc_cls):
     out = torch.empty((S, hq, d), dtype=torch.bfloat16, device=dev)
     ws_bytes = lib.paged_attention_decode_workspace_size(S, hq, hkv, d, maxb * 16,
                                                          args.partition_size)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)    # zeroed once
 
     # one pinned staging buffer per in-flight step: [slots | lens | tables]
     n_i32 = 2 * S + S * maxb
@@ -364,7 +364,7 @@ def run_shared(args, case, torch, lib, alloc_cls):
     k_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
     v_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
     out = torch.empty((S, hq, d), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(1, lib.paged_attention_decode_workspace_size(S, hq, hkv, d, maxb * 16, 0)),
+    ws = torch.zeros(max(1, lib.paged_attention_decode_workspace_size(S, hq, hkv, d, maxb * 16, 0)),
                      dtype=torch.uint8, device=dev)
     ev_pairs, snaps = [], []
     kv_per_tok = 2 * hkv * d * 2

@@ -196,7 +196,12 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *                                  are misread only if a word holds exactly
  *                                  the call's 40-bit tag (tags run in one
  *                                  process-wide sequence from a random start
- *                                  with the top bit set).
+ *                                  with the top bit set).  A workspace
+ *                                  zero-filled when it is allocated and used
+ *                                  with one layout (same num_seqs,
+ *                                  num_q_heads, head_dim and P) is never
+ *                                  misread: no tag is zero, and these words
+ *                                  only ever receive tagged values.
  *                  Piece k of a context is the k-th range it meets.  Calls
  *                  that share a workspace must not overlap in time.
  *                  Returns PKV_ERR_UNSUPPORTED (bf16) when one merge's

@@ -237,7 +237,8 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
         raise ValueError("block_tables [S][max_blocks], context_lens [S]")
     need = paged_attention_decode_workspace_size(S, hq, hkv, d, max_context_len, partition_size)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled once: no arrival word can then hold a call's tag by chance
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _dev(workspace)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
