@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle_pins as P
-from gpu_helpers import LibDecodeState, f64_of, i32, words_of
+from gpu_helpers import LibDecodeState, f64_of, words_of
 from oracle import attention, numerics, paging
 from paged_kv_cache_63_amd import _lib
 from workloads import decode_case, gqa4_decode, long_context_decode, tiny_fp32_decode

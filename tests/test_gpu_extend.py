@@ -7,7 +7,7 @@ import torch
 
 import oracle_pins as P
 from gpu_helpers import f64_of, i32, poisoned_pools, to_dev, words_of
-from oracle import attention, numerics, paging
+from oracle import attention
 from paged_kv_cache_63_amd import BlockAllocator, _lib
 from workloads import extend_case, multiturn_extend
 

@@ -5,8 +5,6 @@ cases it hands back to Python (a sealed block, a short free list) give the
 same result as appending to each sequence in turn.  The randomized
 comparison with the oracle's block manager is in test_allocator.py."""
 
-import ctypes
-
 import numpy as np
 import pytest
 
