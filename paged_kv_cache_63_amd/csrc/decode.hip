@@ -691,7 +691,10 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     // (plain decode: tagged arrival words, nothing to clear; the shared-prefix
     // entry clears its piece counts with its own table)
-    kern<<<a.num_workgroups, NW * kWave, lds, st>>>(a);
+    // the shared-prefix own pass walks many short suffixes: twice as many,
+    // shorter ranges there (four workgroups per CU; measured 1.8% faster
+    // than two, while one, six or eight were slower)
+    kern<<<a.seq_prefix ? 2 * a.num_workgroups : a.num_workgroups, NW * kWave, lds, st>>>(a);
     if (a.seq_prefix) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return -4;
