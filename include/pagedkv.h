@@ -262,13 +262,20 @@ size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t nu
  *                  count, the largest member count and the largest
  *                  group_prefix_blocks (they size the prefix pass's grid)
  *   workspace      at least paged_attention_decode_shared_workspace_size(...)
- *                  bytes, any contents: the paged_attention_decode layout
- *                  (o, m, l pieces and counters), then seq_prefix
- *                  [num_seqs][2] int32 (the block each sequence's own pass
- *                  starts at, and how many prefix partials it folds in), then
- *                  at the next 256-byte boundary the prefix partials o
+ *                  bytes, 8-byte aligned: the paged_attention_decode layout
+ *                  (o, m, l pieces, then one 64-bit word per (sequence, KV
+ *                  head) holding the unit's piece count), then seq_prefix
+ *                  [num_seqs] 64-bit words (the block each sequence's own
+ *                  pass starts at, in bits 0..19, and how many prefix
+ *                  partials it folds in, in bits 20..23), then at the next
+ *                  256-byte boundary the prefix partials o
  *                  [num_seqs][num_q_heads][NS][head_dim], m and l
- *                  [num_seqs][num_q_heads][NS] fp32 (NS key splits).
+ *                  [num_seqs][num_q_heads][NS] fp32 (NS key splits).  Every
+ *                  64-bit word carries the writing call's tag in bits 24..63,
+ *                  as paged_attention_decode's arrival words do, and a word
+ *                  with another tag reads as zero: nothing is cleared
+ *                  between calls, and the same guarantee holds (a workspace
+ *                  zero-filled at allocation is never misread).
  *
  * A member sees the shared blocks up to, not including, the block that holds
  * its last token (that block is always in its own pass): its first
@@ -278,7 +285,9 @@ size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t nu
  * Otherwise the result is undefined, but every access stays inside the pool.  fp32 inputs, or no
  * groups, run paged_attention_decode unchanged.  Errors as
  * paged_attention_decode; PKV_ERR_UNSUPPORTED when the merge weights,
- * 2 x group x (P + NS) + group fp32 words, exceed the LDS.
+ * 2 x group x (P + NS) + group fp32 words, exceed the LDS; PKV_ERR_INVALID
+ * when the prefix splits cover 2^20 blocks or more (the start block would
+ * not fit its 20 bits).
  */
 int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
                                   const void* v_pool, int32_t num_blocks,

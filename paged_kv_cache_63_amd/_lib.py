@@ -279,7 +279,8 @@ def paged_attention_decode_shared(out, q, k_pool, v_pool, block_tables, context_
     need = paged_attention_decode_shared_workspace_size(S, hq, hkv, d, max_context_len,
                                                         partition_size, G, max_size, max_pb)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled: no arrival word or per-sequence word then holds a tag
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _dev(workspace)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

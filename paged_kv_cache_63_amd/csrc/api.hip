@@ -98,7 +98,7 @@ PrefixSplit prefix_split(int32_t num_groups, int32_t max_group_size, int32_t max
   return {(int32_t)blocks, (int32_t)((max_prefix_blocks + blocks - 1) / blocks)};
 }
 
-// A tag per plain decode call for its arrival words (bits 24..63 of a word;
+// A tag per decode call for its arrival words (bits 24..63 of a word;
 // the count of the call's arrived pieces sits below).  Tags come from one
 // process-wide sequence that starts at a random point with its top bit set:
 // a word written by an earlier call carries an earlier tag, and a word the
@@ -118,9 +118,11 @@ struct SharedLayout {
 };
 SharedLayout shared_layout(int64_t S, int64_t hq, int64_t hkv, int64_t D, int64_t P, int64_t NS) {
   SharedLayout l{};
-  const size_t dec = (size_t)S * hq * P * (D + 2) * 4 + (size_t)S * hkv * 4;
+  // the plain decode's layout (pieces, then arrival words), then one tagged
+  // word per sequence (8-byte aligned: D + 2 is even)
+  const size_t dec = (size_t)S * hq * P * (D + 2) * 4 + (size_t)S * hkv * 8;
   l.seq_prefix = dec;
-  const size_t after = dec + (size_t)S * 2 * 4;
+  const size_t after = dec + (size_t)S * 8;
   l.pre_o = (after + 255) / 256 * 256;
   l.pre_m = l.pre_o + (size_t)S * hq * NS * D * 4;
   l.pre_l = l.pre_m + (size_t)S * hq * NS * 4;
@@ -409,10 +411,15 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
     return fail(PKV_ERR_UNSUPPORTED,
                 "max_context_len %d over partition_size %d gives %lld pieces per context; use a "
                 "larger partition_size", max_context_len, ptok, (long long)P);
+  // a sequence's start block travels in 20 bits of its tagged word
+  if ((int64_t)sp.count * sp.blocks >= (1 << 20))
+    return fail(PKV_ERR_INVALID, "max_prefix_blocks %d too large", max_prefix_blocks);
   const SharedLayout lay = shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, P, sp.count);
   if (!workspace || workspace_bytes < lay.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
                 workspace_bytes);
+  if ((uintptr_t)workspace % 8)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 8-byte aligned");
 
   uint8_t* ws = (uint8_t*)workspace;
   pkv::DecodeArgs a{};
@@ -427,7 +434,8 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
     a.part_o = (float*)ws;
     a.part_m = a.part_o + rows * head_dim;
     a.part_l = a.part_m + rows;
-    a.counters = (int32_t*)(a.part_l + rows);
+    a.arrive = (uint64_t*)(a.part_l + rows);
+    a.tag = next_call_tag();
   }
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -439,7 +447,7 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   a.max_partitions = (int32_t)P;
   a.num_workgroups = decode_workgroups();
   a.scale = scale;
-  a.seq_prefix = (int32_t*)(ws + lay.seq_prefix);
+  a.seq_prefix = (uint64_t*)(ws + lay.seq_prefix);
   a.pre_o = (float*)(ws + lay.pre_o);
   a.pre_m = (float*)(ws + lay.pre_m);
   a.pre_l = (float*)(ws + lay.pre_l);
@@ -457,7 +465,8 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   p.pre_o = (float*)a.pre_o;
   p.pre_m = (float*)a.pre_m;
   p.pre_l = (float*)a.pre_l;
-  p.seq_prefix = (int32_t*)a.seq_prefix;
+  p.seq_prefix = (uint64_t*)a.seq_prefix;
+  p.tag = a.tag;
   p.num_groups = num_groups;
   p.max_group_size = max_group_size;
   p.num_seqs = num_seqs;
@@ -471,9 +480,9 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   p.scale = scale;
 
   hipStream_t st = (hipStream_t)stream;
-  // counters and seq_prefix are adjacent: one clear for both
-  rc = pkv::clear_ints(a.counters, (int64_t)num_seqs * (num_kv_heads + 2), st);
-  if (!rc) rc = pkv::launch_prefix(p, st);
+  // nothing to clear: the prefix pass tags the words it writes with this
+  // call's tag, and the decode reads any other word as "no prefix"
+  rc = pkv::launch_prefix(p, st);
   if (!rc) rc = pkv::launch_decode(a, dtype, st);
   return rc ? fail(rc, "shared-prefix decode launch failed: %s", hipGetErrorString(hipGetLastError()))
             : ok();

@@ -73,10 +73,9 @@ struct DecodeArgs {
   float* part_o;   // [S][Hq][P][D]
   float* part_m;   // [S][Hq][P]
   float* part_l;   // [S][Hq][P]
-  int32_t* counters;  // shared-prefix decode: [S][Hkv] pieces per unit
-  // Plain decode: [S][Hkv] arrival words, bits 24..63 a call's tag and bits
-  // 0..23 the pieces of that call arrived so far; a word with another tag
-  // counts as zero, so the words need no clearing between calls.
+  // [S][Hkv] arrival words, bits 24..63 a call's tag and bits 0..23 the
+  // pieces of that call arrived so far; a word with another tag counts as
+  // zero, so the words need no clearing between calls.
   uint64_t* arrive;
   uint64_t tag;       // this call's tag, already in bits 24..63
   int32_t num_blocks;
@@ -91,8 +90,11 @@ struct DecodeArgs {
   float scale;
   // Shared-prefix decode only (null / 0 otherwise): per sequence, the first
   // block its own pass starts at and how many prefix partials (pre_*, one
-  // per key split of the prefix pass) its result folds in.
-  const int32_t* seq_prefix; // [S][2]: start block, number of prefix partials
+  // per key split of the prefix pass) its result folds in, as one word that
+  // the prefix pass writes for each group member: this call's tag in bits
+  // 24..63, the start block in bits 0..19, the partial count in bits 20..23.
+  // A word with another tag (a sequence in no group) means 0 and 0.
+  const uint64_t* seq_prefix; // [S]
   const float* pre_o;        // [S][Hq][num_splits][D]
   const float* pre_m;        // [S][Hq][num_splits]
   const float* pre_l;        // [S][Hq][num_splits]
@@ -100,9 +102,6 @@ struct DecodeArgs {
 };
 
 int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st);
-
-// Zero n int32 words with a kernel (graph-capturable, unlike a memset).
-int clear_ints(int32_t* p, int64_t n, hipStream_t st);
 
 struct ExtendArgs {
   void* out;
@@ -143,7 +142,8 @@ struct PrefixArgs {
   float* pre_o;
   float* pre_m;
   float* pre_l;
-  int32_t* seq_prefix;       // [S][2]
+  uint64_t* seq_prefix;      // [S] tagged words, as DecodeArgs::seq_prefix
+  uint64_t tag;              // the decode call's tag (bits 24..63)
   int32_t num_groups;
   int32_t max_group_size;
   int32_t num_seqs;

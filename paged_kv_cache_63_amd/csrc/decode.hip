@@ -22,6 +22,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr size_t kDecodeLdsMax = 160 * 1024 - 256;   // dynamic LDS: a CU's 160 KB less the static part
 constexpr int kBs = 16;  // tokens per block
+constexpr uint64_t kTagLow = (1ull << 24) - 1;   // bits below a call's tag
 
 __device__ __forceinline__ float wave_xor(float x, int mask) {
   return __shfl_xor(x, mask, kWave);
@@ -141,10 +142,17 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   const int w = blockIdx.x;
   uint16_t* out = (uint16_t*)a.out;
   // Shared-prefix decode: sequence s's own pass covers its blocks from
-  // start_block(s) on (the prefix pass covers those before).
+  // start_block(s) on (the prefix pass covers those before); the start
+  // block sits in the sequence's word, which counts only if the prefix pass
+  // of this call wrote it.
   auto start_block = [&](int s, int nb) {
-    if constexpr (SHARED) return min(a.seq_prefix[2 * s], max(nb - 1, 0));
-    else return 0;
+    if constexpr (SHARED) {
+      const uint64_t v = a.seq_prefix[s];
+      const int st = (v & ~kTagLow) == a.tag ? (int)(v & 0xfffff) : 0;
+      return min(st, max(nb - 1, 0));
+    } else {
+      return 0;
+    }
   };
   auto nblocks = [&](int s) {
     const int nb = (usable_len(a, s) + kBs - 1) / kBs;
@@ -321,8 +329,8 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
         }
       }
     }
-    if constexpr (SHARED)
-      if (k == 0 && tid == 0) a.counters[(int64_t)s * hkv + h] = np;   // pieces of the unit
+    if constexpr (SHARED)   // pieces of the unit, for the fold kernel
+      if (k == 0 && tid == 0) a.arrive[(int64_t)s * hkv + h] = a.tag | (uint64_t)np;
   };
 
   // Merge all np pieces of unit (s, h) (called by the piece that arrived
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
     // count this piece in: a word that carries another call's tag holds
     // no arrival of this call
     uint64_t* w = &a.arrive[(int64_t)pend_s[tid] * hkv + pend_h[tid]];
-    constexpr uint64_t kCount = (1ull << 24) - 1;
+    constexpr uint64_t kCount = kTagLow;
     uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint64_t prev;
     while (true) {
@@ -591,18 +599,13 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 
-// Clears the shared-prefix decode's piece counts (and the per-sequence
-// prefix table beside them) before its kernels fill them (a kernel rather
-// than a memset, so the call can be captured in a graph).
-__global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* c, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) c[i] = 0;
-}
-
 // Shared-prefix decode, last step: for every (sequence, KV head) the pieces
 // of the sequence's own pass and the prefix pass's partials are combined by
 // the log-sum-exp rule, out = sum_j o_j l_j e^(m_j - M) / sum_j l_j e^(m_j - M)
-// (natural-log statistics).  A unit whose context is empty (piece count 0)
-// was given its zero rows by the decode kernel.
+// (natural-log statistics).  The unit's piece count and the sequence's
+// prefix-partial count come from words tagged by this call's kernels; a
+// word with another tag means 0 (a unit with an empty context, which the
+// decode kernel gave its zero rows, or a sequence in no group).
 template <int D>
 __global__ __launch_bounds__(256) void decode_fold_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float fold_s[];   // [g][n] m, [g][n] weights, [g] 1/sum
@@ -612,11 +615,13 @@ __global__ __launch_bounds__(256) void decode_fold_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int s = unit / hkv;
   const int h = unit - s * hkv;
-  const int np = a.counters[unit];
+  const uint64_t cw = a.arrive[unit];
+  const int np = (cw & ~kTagLow) == a.tag ? (int)(cw & kTagLow) : 0;
   if (np <= 0) return;
   const int NS = a.num_splits;
   const int P = a.max_partitions;
-  const int nsp = min(max(a.seq_prefix[2 * s + 1], 0), NS);
+  const uint64_t pw = a.seq_prefix[s];
+  const int nsp = (pw & ~kTagLow) == a.tag ? min((int)((pw >> 20) & 0xf), NS) : 0;
   const int n = np + nsp;
   const int tid = threadIdx.x;
   for (int idx = tid; idx < g * n; idx += 256) {
@@ -689,8 +694,7 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
       attr_set[a.seq_prefix != nullptr] = true;
     }
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
-    // (plain decode: tagged arrival words, nothing to clear; the shared-prefix
-    // entry clears its piece counts with its own table)
+    // (tagged words, nothing to clear)
     // the shared-prefix own pass walks many short suffixes: twice as many,
     // shorter ranges there (four workgroups per CU; measured 1.8% faster
     // than two, while one, six or eight were slower)
@@ -726,13 +730,6 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
 }
 
 }  // namespace
-
-int clear_ints(int32_t* p, int64_t n, hipStream_t st) {
-  if (n <= 0) return 0;
-  const int64_t cgrid = (n + 255) / 256;
-  clear_counters_kernel<<<(int)(cgrid < 1024 ? cgrid : 1024), 256, 0, st>>>(p, n);
-  return status_of(hipGetLastError());
-}
 
 int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
   if (a.num_seqs == 0) return 0;

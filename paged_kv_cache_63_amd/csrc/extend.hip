@@ -201,8 +201,9 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
         const int s = a.group_seqs[goff + m];
         if (s < 0 || s >= a.num_seqs) continue;
         const int Ls = a.context_lens[s];
-        a.seq_prefix[2 * s] = Ls >= 1 ? min(pblk, (Ls - 1) / kBs) : 0;
-        a.seq_prefix[2 * s + 1] = Ls >= 1 ? (pblk + a.split_blocks - 1) / a.split_blocks : 0;
+        const uint64_t start = Ls >= 1 ? min(pblk, (Ls - 1) / kBs) : 0;
+        const uint64_t nsp = Ls >= 1 ? (pblk + a.split_blocks - 1) / a.split_blocks : 0;
+        a.seq_prefix[s] = a.tag | (nsp << 20) | start;
       }
     }
     const int klo = split * a.split_blocks * kBs;

@@ -167,3 +167,25 @@ def test_no_groups_is_plain_decode(case):
     none = (i32([0]), i32([0]), i32(np.zeros(0, np.int32)), 0, 0)
     got, _ = _shared(lib, scale, none)
     assert np.abs(got - want).max() <= 2e-2
+
+
+@pytest.mark.parametrize("partition_size", [0, 64])
+def test_workspace_reused_with_other_groups(case, partition_size):
+    """One workspace, two calls: both families grouped, then only PB's.  The
+    members of PA's family decode on their own in the second call; their
+    per-sequence words still hold what the first call's prefix pass wrote,
+    which the second call must not take for its own."""
+    lib, ref, scale, want = case
+    names = lib["names"]
+    both = _explicit_groups(names)
+    idx = {n: i for i, n in enumerate(names)}
+    only_b = (i32([0, 4]), i32([idx[n] for n in ("PB", "B0", "B1", "B2")]), i32([8]), 4, 8)
+    mx = int(lib["lens"].max())
+    need = max(_lib.paged_attention_decode_shared_workspace_size(
+        len(names), HQ, HKV, D, mx, partition_size, len(g[2]), g[3], g[4]) for g in (both, only_b))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for groups in (both, only_b, both):
+        got, _ = _shared(lib, scale, groups, partition_size, ws)
+        err = np.abs(got - want).max()
+        print("groups", len(groups[2]), "partition", partition_size, "max err", err)
+        assert np.isfinite(got).all() and err <= 2e-2, err

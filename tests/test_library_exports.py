@@ -117,7 +117,8 @@ def test_empty_calls_are_no_ops(lib):
 
 
 def test_shared_workspace_layout(lib):
-    """The plain decode's regions, then seq_prefix [S][2] int32, then at the
+    """The plain decode's regions (pieces, then one 64-bit arrival word per
+    (sequence, KV head)), then seq_prefix [S] 64-bit words, then at the
     next 256-byte boundary the prefix partials o [S][Hq][NS][D], m, l.  NS:
     the prefix pass aims at one workgroup per compute unit (256 on MI355X,
     also the value used where no device is visible): 268 members x 4 heads =
@@ -126,8 +127,8 @@ def test_shared_workspace_layout(lib):
     ws = lib.paged_attention_decode_shared_workspace_size
     S, hq, hkv, D = 268, 32, 8, 128
     P = 5200 // 512 + 1 + 1
-    dec = S * hq * P * (D + 2) * 4 + S * hkv * 4
-    pre_o = -(-(dec + S * 2 * 4) // 256) * 256
+    dec = S * hq * P * (D + 2) * 4 + S * hkv * 8
+    pre_o = -(-(dec + S * 8) // 256) * 256
     NS = 6
     assert ws(S, hq, hkv, D, 5200, 512, 1, 268, 256) == pre_o + S * hq * NS * (D + 2) * 4
     # many groups: one split each
@@ -161,3 +162,13 @@ def test_shared_bad_arguments_rejected(lib):
     rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 4, one, 2, 64, 32, 8, 128,
                                            16, f, one, one, one, -1, 2, 2, 0, null, 0, 1, None)
     assert rc == -1
+    # a workspace not 8-byte aligned (it holds 64-bit tagged words)
+    rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 4, one, 2, 64, 32, 8, 128,
+                                           16, f, one, one, one, 1, 2, 2, 0, ctypes.c_void_p(12),
+                                           1 << 40, 1, None)
+    assert rc == -3 and b"aligned" in lib.paged_kv_last_error()
+    # a start block that does not fit the 20 bits of its word
+    rc = lib.paged_attention_decode_shared(one, one, one, one, 10, one, 1 << 21, one, 2, 64, 32, 8,
+                                           128, 16, f, one, one, one, 1, 2, 1 << 20, 0, one,
+                                           1 << 40, 1, None)
+    assert rc == -1 and b"max_prefix_blocks" in lib.paged_kv_last_error()
