@@ -50,7 +50,8 @@ __device__ __forceinline__ int usable_len(const DecodeArgs& a, int s) {
 // Balanced split: the work of the call is the list of (sequence, KV head,
 // block) triples, sequence-major; unit (s, h) owns nb(s) = ceil(L_s / 16)
 // consecutive positions of that list.  The grid has a fixed number W of
-// workgroups (two per compute unit, the number that are resident at once)
+// workgroups (the number resident at once: two 8-wave ones per compute
+// unit, eight 2-wave ones in the shared-prefix own pass)
 // and workgroup w takes positions [w*C, (w+1)*C) with
 // C = max(partition_blocks, ceil(total / W)), so every workgroup streams
 // the same number of K/V blocks and all of them finish together (a grid of
@@ -676,16 +677,22 @@ template <int D>
 int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
   const int g = a.num_q_heads / a.num_kv_heads;
   if (dtype == 1) {
-    constexpr int NW = 8;
-    // wave-merge area [NW][g][D] + [NW][16] m + [NW][16] l, also used for
+    // Plain decode: 8-wave workgroups, two per CU.  The shared-prefix own
+    // pass walks many short suffixes (tens of blocks): there 2-wave
+    // workgroups, eight per CU, so that a piece is spread over fewer waves
+    // and each wave streams longer (measured: 188-190 us per call against
+    // 200 for 8 waves x 4 per CU, 191 for 4 waves x 4, 194 for 1 wave x 16).
+    constexpr int NW = 8, NWS = 2;
+    const int nw = a.seq_prefix ? NWS : NW;
+    // wave-merge area [nw][g][D] + [nw][16] m + [nw][16] l, also used for
     // the piece weights of a merge ([2][g][P] + [g])
     // (the shared-prefix variant merges in a separate kernel)
-    const size_t wave_area = (size_t)NW * g * D + 2 * NW * 16;
+    const size_t wave_area = (size_t)nw * g * D + 2 * nw * 16;
     const size_t merge_area = (size_t)2 * g * a.max_partitions + g;
     const size_t words = a.seq_prefix ? wave_area : max(wave_area, merge_area);
     const size_t lds = words * sizeof(float);
     if (lds > kDecodeLdsMax) return -2;
-    auto kern = a.seq_prefix ? decode_bf16_kernel<D, NW, true> : decode_bf16_kernel<D, NW, false>;
+    auto kern = a.seq_prefix ? decode_bf16_kernel<D, NWS, true> : decode_bf16_kernel<D, NW, false>;
     static bool attr_set[2] = {false, false};   // dynamic LDS above 64 KB needs the limit raised once
     if (!attr_set[a.seq_prefix != nullptr]) {
       if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -695,10 +702,7 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     }
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     // (tagged words, nothing to clear)
-    // the shared-prefix own pass walks many short suffixes: twice as many,
-    // shorter ranges there (four workgroups per CU; measured 1.8% faster
-    // than two, while one, six or eight were slower)
-    kern<<<a.seq_prefix ? 2 * a.num_workgroups : a.num_workgroups, NW * kWave, lds, st>>>(a);
+    kern<<<a.seq_prefix ? 4 * a.num_workgroups : a.num_workgroups, nw * kWave, lds, st>>>(a);
     if (a.seq_prefix) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return -4;
