@@ -67,14 +67,17 @@ int64_t max_pieces(int32_t max_context_len, int32_t ptok) {
 // Two workgroups per compute unit: what the bf16 decode kernel keeps
 // resident at once (cached per device).
 int decode_workgroups() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];   // zero-initialised (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  if (dev < 64 && cached[dev]) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (dev < 64) cached[dev] = 2 * cus;
+  if (dev < 64) cached[dev].store(2 * cus, std::memory_order_relaxed);
   return 2 * cus;
 }
 

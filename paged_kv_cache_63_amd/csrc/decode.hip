@@ -13,6 +13,8 @@
 // partition: out = sum_p o_p l_p e^(m_p-M) / sum_p l_p e^(m_p-M).
 #include <math.h>
 
+#include <atomic>
+
 #include "common.h"
 
 namespace pkv {
@@ -600,6 +602,21 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 
+// Raises a kernel's dynamic-LDS limit to the CU's 160 KB (needed above 64
+// KB) once per device; *done holds one bit per device id below 64 (ids from
+// 64 on set it on every call).  Safe to call from several host threads.
+int raise_lds_limit(const void* kern, std::atomic<uint64_t>* done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -4;
+  const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;
+  if (bit && (done->load(std::memory_order_acquire) & bit)) return 0;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLdsMax) !=
+      hipSuccess)
+    return -4;
+  done->fetch_or(bit, std::memory_order_release);
+  return 0;
+}
+
 // Shared-prefix decode, last step: for every (sequence, KV head) the pieces
 // of the sequence's own pass and the prefix pass's partials are combined by
 // the log-sum-exp rule, out = sum_j o_j l_j e^(m_j - M) / sum_j l_j e^(m_j - M)
@@ -693,13 +710,8 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     const size_t lds = words * sizeof(float);
     if (lds > kDecodeLdsMax) return -2;
     auto kern = a.seq_prefix ? decode_bf16_kernel<D, NWS, true> : decode_bf16_kernel<D, NW, false>;
-    static bool attr_set[2] = {false, false};   // dynamic LDS above 64 KB needs the limit raised once
-    if (!attr_set[a.seq_prefix != nullptr]) {
-      if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kDecodeLdsMax) != hipSuccess)
-        return -4;
-      attr_set[a.seq_prefix != nullptr] = true;
-    }
+    static std::atomic<uint64_t> attr_set[2];   // per variant, one bit per device
+    if (raise_lds_limit((const void*)kern, &attr_set[a.seq_prefix != nullptr])) return -4;
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     // (tagged words, nothing to clear)
     kern<<<a.seq_prefix ? 4 * a.num_workgroups : a.num_workgroups, nw * kWave, lds, st>>>(a);
@@ -708,14 +720,8 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
       if (e != hipSuccess) return -4;
       const size_t flds = (size_t)(2 * g * (a.max_partitions + a.num_splits) + g) * sizeof(float);
       if (flds > kDecodeLdsMax) return -2;
-      static bool fold_attr = false;
-      if (!fold_attr) {
-        if (hipFuncSetAttribute((const void*)decode_fold_kernel<D>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)kDecodeLdsMax) != hipSuccess)
-          return -4;
-        fold_attr = true;
-      }
+      static std::atomic<uint64_t> fold_attr;
+      if (raise_lds_limit((const void*)decode_fold_kernel<D>, &fold_attr)) return -4;
       decode_fold_kernel<D><<<(unsigned)units, 256, flds, st>>>(a);
     }
     return status_of(hipGetLastError());
