@@ -8,9 +8,12 @@ through one pool.  One step is the whole path for one new token per
 sequence:
 
   host   block manager appends a token to every sequence (slots, new blocks,
-         copy-on-write pairs, block tables)  -> one pinned host->device copy
+         copy-on-write pairs, block tables)
   device copy_blocks (when the step produced copy-on-write pairs)
-         paged_kv_append (the new token's K/V into its slot)
+         upload_and_append_tables: the step's slots, lengths and each
+           sequence's last table entry (the only one a decode step can
+           change) read from pinned host memory into the device-resident
+           tables, and the new token's K/V written into its slot, one launch
          paged_attention_decode (pass 1 + the log-sum-exp merge)
 
 Contexts grow by one token per step, as in a real decode loop.  All inputs
@@ -188,16 +191,20 @@ def run_decode(args, case, torch, lib, alloc_cls):
                                                          args.partition_size)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)    # zeroed once
 
-    # one pinned staging buffer per in-flight step: [slots | lens | tables]
-    n_i32 = 2 * S + S * maxb
+    # The block tables stay resident on the device; a decode step changes at
+    # most each sequence's last entry (a fresh block, or a copy-on-write
+    # replacement), so one pinned staging buffer per in-flight step carries
+    # [slots | lens | (index, value) of every sequence's last entry].
+    n_i32 = 4 * S
     ring = [torch.empty(n_i32, dtype=torch.int32, pin_memory=True) for _ in range(3)]
     ring_np = [r.numpy() for r in ring]
     ring_ev = [torch.cuda.Event() for _ in range(3)]
     for e in ring_ev:
         e.record()
-    stage = torch.empty(n_i32, dtype=torch.int32, device=dev)
+    stage = torch.empty(2 * S, dtype=torch.int32, device=dev)
     lens_d = stage[S:2 * S]
-    tables_d = stage[2 * S:].view(S, maxb)
+    tables_d = torch.from_numpy(alloc.tables[:S]).to(dev)
+    rows_s = np.arange(S)
     torch.cuda.synchronize()
 
     kv_per_tok = 2 * hkv * d * 2
@@ -210,12 +217,17 @@ def run_decode(args, case, torch, lib, alloc_cls):
         ring_ev[r].synchronize()
         buf = ring_np[r]
         buf[:S] = sl
-        buf[S:2 * S] = alloc.lens[:S]
-        buf[2 * S:] = alloc.tables[:S].reshape(-1)
+        lens = alloc.lens[:S]
+        buf[S:2 * S] = lens
+        last = (lens - 1) // 16
+        buf[2 * S::2] = rows_s * maxb + last
+        buf[2 * S + 1::2] = alloc.tables[rows_s, last]
         if len(pairs):                                                       # a3
             lib.copy_blocks(k_pool, v_pool, torch.from_numpy(pairs).to(dev))
-        # a2, with the step's index arrays going up in the same launch
-        lib.upload_and_append(stage, ring[r], k_steps[i], v_steps[i], k_pool, v_pool)
+        # a2, with the step's index arrays and table entries going up in the
+        # same launch
+        lib.upload_and_append(stage, ring[r], k_steps[i], v_steps[i], k_pool, v_pool,
+                              tables=tables_d, num_updates=S)
         ring_ev[r].record()
         mcl = int(alloc.lens[:S].max())
         # the decode call is bracketed by timing events on every event_every-th
@@ -248,7 +260,7 @@ def run_decode(args, case, torch, lib, alloc_cls):
     if getattr(args, "keep_state", False):     # for tests of this loop: what the last step saw
         res["state"] = dict(out=out, q=q_steps[T - 1], k_new=k_steps[T - 1], v_new=v_steps[T - 1],
                             k_pool=k_pool, v_pool=v_pool, tables=alloc.tables[:S].copy(),
-                            lens=alloc.lens[:S].copy())
+                            lens=alloc.lens[:S].copy(), tables_dev=tables_d.cpu().numpy())
     return res
 
 
@@ -369,16 +381,18 @@ def run_shared(args, case, torch, lib, alloc_cls):
     ev_pairs, snaps = [], []
     kv_per_tok = 2 * hkv * d * 2
     n_pairs = 0
-    # pinned staging per in-flight step: [slots | lens | tables], uploaded by a kernel
-    n_i32 = 2 * S + S * maxb
+    # device-resident tables; pinned staging per in-flight step: [slots | lens
+    # | (index, value) of every sequence's last table entry], uploaded by a kernel
+    n_i32 = 4 * S
     ring = [torch.empty(n_i32, dtype=torch.int32, pin_memory=True) for _ in range(3)]
     ring_np = [r.numpy() for r in ring]
     ring_ev = [torch.cuda.Event() for _ in range(3)]
     for e in ring_ev:
         e.record()
-    stage = torch.empty(n_i32, dtype=torch.int32, device=dev)
+    stage = torch.empty(2 * S, dtype=torch.int32, device=dev)
     lens_d = stage[S:2 * S]
-    tables_d = stage[2 * S:].view(S, maxb)
+    tables_d = torch.from_numpy(alloc.tables[rows]).to(dev)
+    rows_s = np.arange(S)
     groups = None
     if not args.plain_decode:
         # the shared prompt's blocks lead every table for the whole run: the
@@ -402,8 +416,11 @@ def run_shared(args, case, torch, lib, alloc_cls):
         buf = ring_np[r]
         buf[:S] = slots
         buf[S:2 * S] = lens
-        buf[2 * S:] = alloc.tables[rows].reshape(-1)
-        lib.upload_and_append(stage, ring[r], k_steps[i], v_steps[i], k_pool, v_pool)
+        last = (lens - 1) // 16
+        buf[2 * S::2] = rows_s * maxb + last
+        buf[2 * S + 1::2] = alloc.tables[rows, last]
+        lib.upload_and_append(stage, ring[r], k_steps[i], v_steps[i], k_pool, v_pool,
+                              tables=tables_d, num_updates=S)
         ring_ev[r].record()
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

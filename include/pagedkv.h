@@ -402,6 +402,37 @@ int upload_and_append(void* dst, const void* staging, int64_t bytes, int64_t slo
                       int32_t block_size, int32_t dtype, void* stream);
 
 /*
+ * upload_and_append_tables -- upload_and_append for a caller that keeps its
+ * block tables resident on the device and sends only the entries a step
+ * changed.  In a decode step only a sequence's last table entry can change
+ * (a fresh block when the last one is full, or its copy-on-write
+ * replacement: "Paged Attention for Efficient Memory Management", The Daily
+ * Triptych, "The story" and technical summary), so a step's update is one
+ * (index, value) pair per sequence instead of the whole table.
+ *
+ *   dst, staging, bytes, slots_offset, and the append arguments
+ *                 as upload_and_append
+ *   block_tables  device int32 array of table_words words (for example the
+ *                 [num_seqs][max_blocks_per_seq] tables a decode call reads)
+ *   num_updates   >= 0 pairs of int32 (index, value), stored in staging right
+ *                 after its first `bytes` bytes (bytes a multiple of 4);
+ *                 block_tables[index] = value, indexes outside
+ *                 [0, table_words) are skipped.  Pairs with the same index
+ *                 leave one of their values, unspecified which.
+ *
+ * The table writes happen in the same launch as the upload (from 512 tokens
+ * on, in the upload launch that precedes the bulk append) and are complete
+ * for every later call on `stream`.  Errors as upload_and_append, plus
+ * PKV_ERR_INVALID for negative counts, or updates without block_tables or
+ * with bytes not a multiple of 4.
+ */
+int upload_and_append_tables(void* dst, const void* staging, int64_t bytes, int64_t slots_offset,
+                             int32_t* block_tables, int64_t table_words, int32_t num_updates,
+                             const void* k_new, const void* v_new, int32_t num_tokens,
+                             void* k_pool, void* v_pool, int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
+
+/*
  * block_manager_append_step -- HOST call, the one exception to the device
  * conventions above: every pointer is host memory, nothing is enqueued and
  * no GPU is touched.  The decode step of the host block manager: one new

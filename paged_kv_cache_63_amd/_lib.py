@@ -23,7 +23,7 @@ SYMBOLS = ("paged_kv_append", "copy_blocks", "swap_blocks", "paged_attention_dec
            "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
            "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
            "paged_kv_last_error", "block_manager_append_step", "pinned_upload",
-           "upload_and_append")
+           "upload_and_append", "upload_and_append_tables")
 
 
 class PagedKVError(RuntimeError):
@@ -69,6 +69,10 @@ def load():
     lib.upload_and_append.restype = ctypes.c_int
     lib.upload_and_append.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, p, p, i32, p, p, i32,
                                       i32, i32, i32, i32, p]
+    lib.upload_and_append_tables.restype = ctypes.c_int
+    lib.upload_and_append_tables.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, p,
+                                             ctypes.c_int64, i32, p, p, i32, p, p, i32, i32, i32,
+                                             i32, i32, p]
     lib.block_manager_append_step.restype = ctypes.c_int
     lib.block_manager_append_step.argtypes = [p, p, p, p, p, i32, i32, p, p, i32, i32, p, i32,
                                               p, p, p, p, p]
@@ -169,10 +173,16 @@ def pinned_upload(dst, src, nbytes=None):
     _check(load().pinned_upload(_ptr(dst), _ptr(src), n, _stream()))
 
 
-def upload_and_append(dst, staging, k_new, v_new, k_pool, v_pool, slots_at=0):
+def upload_and_append(dst, staging, k_new, v_new, k_pool, v_pool, slots_at=0, tables=None,
+                      num_updates=0):
     """:func:`pinned_upload` of the int32 ``staging`` buffer into ``dst`` and
     :func:`paged_kv_append` of ``k_new``/``v_new`` whose slot mapping is
-    ``staging[slots_at : slots_at + len(k_new)]``, in one call."""
+    ``staging[slots_at : slots_at + len(k_new)]``, in one call.
+
+    With ``tables`` (a device int32 tensor) and ``num_updates`` > 0, the last
+    ``2 * num_updates`` words of ``staging`` are (index, value) pairs written
+    into ``tables.view(-1)`` in the same launch, and only the words before
+    them are copied to ``dst``."""
     nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
     _dev(k_new, v_new, k_pool, v_pool)
     if not dst.is_cuda or not (staging.is_cuda or staging.is_pinned()):
@@ -184,12 +194,24 @@ def upload_and_append(dst, staging, k_new, v_new, k_pool, v_pool, slots_at=0):
         raise ValueError("k_new/v_new must be [T][Hkv][D]")
     if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
         raise ValueError("k_new/v_new dtype must match the pools")
-    n = staging.numel() * 4
+    nu = int(num_updates)
+    if nu < 0 or 2 * nu > staging.numel():
+        raise ValueError("num_updates must be in [0, staging.numel() / 2]")
+    if nu and (tables is None or not tables.is_cuda or tables.dtype != torch.int32
+               or not tables.is_contiguous()):
+        raise ValueError("table updates need a contiguous int32 device tensor of tables")
+    n = (staging.numel() - 2 * nu) * 4
     if n > dst.numel() * dst.element_size():
-        raise ValueError("dst is smaller than staging")
-    _check(load().upload_and_append(_ptr(dst), _ptr(staging), n, 4 * int(slots_at), _ptr(k_new),
-                                    _ptr(v_new), T, _ptr(k_pool), _ptr(v_pool), nb, hkv, d, bs,
-                                    dt, _stream()))
+        raise ValueError("dst is smaller than the staged words")
+    if nu == 0:
+        _check(load().upload_and_append(_ptr(dst), _ptr(staging), n, 4 * int(slots_at),
+                                        _ptr(k_new), _ptr(v_new), T, _ptr(k_pool), _ptr(v_pool),
+                                        nb, hkv, d, bs, dt, _stream()))
+        return
+    _check(load().upload_and_append_tables(_ptr(dst), _ptr(staging), n, 4 * int(slots_at),
+                                           _ptr(tables), tables.numel(), nu, _ptr(k_new),
+                                           _ptr(v_new), T, _ptr(k_pool), _ptr(v_pool), nb, hkv,
+                                           d, bs, dt, _stream()))
 
 
 def new_host_pools(num_blocks, num_kv_heads, head_dim, block_size=16, dtype=torch.bfloat16):

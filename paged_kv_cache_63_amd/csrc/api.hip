@@ -232,18 +232,22 @@ int pinned_upload(void* dst, const void* src, int64_t bytes, void* stream) {
   return rc ? fail(rc, "upload launch failed") : ok();
 }
 
-int upload_and_append(void* dst, const void* staging, int64_t bytes, int64_t slots_offset,
-                      const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
-                      void* v_pool, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t block_size, int32_t dtype, void* stream) {
+int upload_and_append_tables(void* dst, const void* staging, int64_t bytes, int64_t slots_offset,
+                             int32_t* block_tables, int64_t table_words, int32_t num_updates,
+                             const void* k_new, const void* v_new, int32_t num_tokens,
+                             void* k_pool, void* v_pool, int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
   int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
   if (rc) return rc;
-  if (bytes < 0 || num_tokens < 0 || num_blocks <= 0)
-    return fail(PKV_ERR_INVALID, "bad bytes/num_tokens/num_blocks");
+  if (bytes < 0 || num_tokens < 0 || num_blocks <= 0 || num_updates < 0 || table_words < 0)
+    return fail(PKV_ERR_INVALID, "bad bytes/num_tokens/num_blocks/num_updates/table_words");
   if (slots_offset < 0 || slots_offset % 4 || slots_offset + 4 * (int64_t)num_tokens > bytes)
     return fail(PKV_ERR_INVALID, "slot mapping (offset %lld, %d tokens) not inside the %lld staged bytes",
                 (long long)slots_offset, num_tokens, (long long)bytes);
-  if (bytes == 0) return ok();
+  if (num_updates > 0 && (bytes % 4 || !block_tables))
+    return fail(PKV_ERR_INVALID, "table updates need block_tables and a staged size that is a "
+                "multiple of 4 (%lld)", (long long)bytes);
+  if (bytes == 0 && num_updates == 0) return ok();
   if (!dst || !staging) return fail(PKV_ERR_INVALID, "null pointer argument");
   if (num_tokens > 0 && (!k_new || !v_new || !k_pool || !v_pool))
     return fail(PKV_ERR_INVALID, "null pointer argument");
@@ -251,10 +255,29 @@ int upload_and_append(void* dst, const void* staging, int64_t bytes, int64_t slo
   void* sv = nullptr;
   if (device_view(dst, &d) || device_view(staging, &sv))
     return fail(PKV_ERR_INVALID, "buffers must be device memory or pinned host memory");
+  pkv::TableUpdates u;
+  if (num_updates > 0) {
+    void* tv = nullptr;
+    if (device_view(block_tables, &tv))
+      return fail(PKV_ERR_INVALID, "block_tables must be device memory");
+    u.table = (int32_t*)tv;
+    u.words = table_words;
+    u.pairs = (const int32_t*)((const uint8_t*)sv + bytes);
+    u.n = num_updates;
+  }
   rc = pkv::launch_upload_append(d, sv, bytes, slots_offset, k_new, v_new, num_tokens, k_pool,
                                  v_pool, num_blocks, num_kv_heads, head_dim, elem_bytes(dtype),
-                                 (hipStream_t)stream);
+                                 (hipStream_t)stream, u);
   return rc ? fail(rc, "upload_and_append launch failed") : ok();
+}
+
+int upload_and_append(void* dst, const void* staging, int64_t bytes, int64_t slots_offset,
+                      const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
+                      void* v_pool, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t dtype, void* stream) {
+  return upload_and_append_tables(dst, staging, bytes, slots_offset, nullptr, 0, 0, k_new, v_new,
+                                  num_tokens, k_pool, v_pool, num_blocks, num_kv_heads, head_dim,
+                                  block_size, dtype, stream);
 }
 
 int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,

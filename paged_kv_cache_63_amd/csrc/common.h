@@ -49,11 +49,21 @@ int launch_append(const void* k_new, const void* v_new, const int32_t* slots, in
 int launch_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, const int32_t* mapping,
                        int32_t num_pairs, int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
                        hipStream_t st);
-int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st);
+// Block-table entries written by an upload kernel: table[pairs[2i]] =
+// pairs[2i + 1], i < n (pairs device-readable; none when n is 0).
+struct TableUpdates {
+  int32_t* table = nullptr;
+  int64_t words = 0;
+  const int32_t* pairs = nullptr;
+  int64_t n = 0;
+};
+
+int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st,
+                  TableUpdates u = TableUpdates{});
 int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slots_offset,
                          const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
                          void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d,
-                         int32_t elem_bytes, hipStream_t st);
+                         int32_t elem_bytes, hipStream_t st, TableUpdates u = TableUpdates{});
 int launch_swap_blocks(void* dst_k, void* dst_v, int32_t num_dst, const void* src_k,
                        const void* src_v, int32_t num_src, const int32_t* mapping,
                        int32_t num_pairs, int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,

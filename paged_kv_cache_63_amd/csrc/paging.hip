@@ -274,10 +274,22 @@ __device__ __forceinline__ void upload_bytes(uint8_t* __restrict__ dst,
   for (int64_t i = done + t0; i < bytes; i += stride) dst[i] = src[i];
 }
 
+// Block-table updates that travel with an upload: table[pairs[2i]] =
+// pairs[2i + 1] for i < n (the pairs read through the staging buffer's
+// device mapping); an index outside [0, words) is skipped.
+__device__ __forceinline__ void apply_updates(const TableUpdates& u, int64_t wg, int64_t nwg) {
+  for (int64_t i = wg * kThreads + threadIdx.x; i < u.n; i += nwg * kThreads) {
+    const int32_t idx = u.pairs[2 * i];
+    const int32_t val = u.pairs[2 * i + 1];
+    if (idx >= 0 && idx < u.words) u.table[idx] = val;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void upload_kernel(uint8_t* __restrict__ dst,
                                                           const uint8_t* __restrict__ src,
-                                                          int64_t bytes, int vec) {
+                                                          int64_t bytes, int vec, TableUpdates u) {
   upload_bytes(dst, src, bytes, vec, blockIdx.x, gridDim.x);
+  apply_updates(u, blockIdx.x, gridDim.x);
 }
 
 // A decode step's host->device traffic in one launch: workgroups
@@ -290,10 +302,12 @@ __global__ __launch_bounds__(kThreads) void upload_append_kernel(
     uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int64_t bytes, int vec,
     int32_t up_wgs, const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
     const int32_t* __restrict__ slots, int64_t pieces, int32_t pieces_per_row, int32_t hkv,
-    int32_t d, int32_t num_blocks, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool) {
-  if ((int32_t)blockIdx.x < up_wgs)
+    int32_t d, int32_t num_blocks, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    TableUpdates u) {
+  if ((int32_t)blockIdx.x < up_wgs) {
     upload_bytes(dst, src, bytes, vec, blockIdx.x, up_wgs);
-  else
+    apply_updates(u, blockIdx.x, up_wgs);
+  } else
     append_pieces<E>(k_new, v_new, slots, pieces, pieces_per_row, hkv, d, 16, num_blocks, k_pool,
                      v_pool, blockIdx.x - up_wgs, gridDim.x - up_wgs);
 }
@@ -474,27 +488,28 @@ static int64_t upload_grid(int64_t bytes, int vec) {
   return g < 1 ? 1 : (g > 1024 ? 1024 : g);
 }
 
-int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st) {
+int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st, TableUpdates u) {
   const int vec = upload_vec(dst, src);
-  upload_kernel<<<(unsigned)upload_grid(bytes, vec), kThreads, 0, st>>>(
-      (uint8_t*)dst, (const uint8_t*)src, bytes, vec);
+  const int64_t g = max(upload_grid(bytes, vec), min((u.n + kThreads - 1) / kThreads, (int64_t)1024));
+  upload_kernel<<<(unsigned)max(g, (int64_t)1), kThreads, 0, st>>>(
+      (uint8_t*)dst, (const uint8_t*)src, bytes, vec, u);
   return status_of(hipGetLastError());
 }
 
 int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slots_offset,
                          const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
                          void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d,
-                         int32_t elem_bytes, hipStream_t st) {
-  if (num_tokens == 0) return bytes > 0 ? launch_upload(dst, src, bytes, st) : 0;
+                         int32_t elem_bytes, hipStream_t st, TableUpdates u) {
+  if (num_tokens == 0) return bytes > 0 || u.n > 0 ? launch_upload(dst, src, bytes, st, u) : 0;
   if (num_tokens >= kBulkTokens) {
     // bulk: the window scans read the slots many times, from the device copy
-    int rc = bytes > 0 ? launch_upload(dst, src, bytes, st) : 0;
+    int rc = bytes > 0 || u.n > 0 ? launch_upload(dst, src, bytes, st, u) : 0;
     if (rc) return rc;
     return launch_append(k_new, v_new, (const int32_t*)((const uint8_t*)dst + slots_offset),
                          num_tokens, k_pool, v_pool, num_blocks, hkv, d, 16, elem_bytes, st);
   }
   const int vec = upload_vec(dst, src);
-  const int64_t up = upload_grid(bytes, vec);
+  const int64_t up = max(upload_grid(bytes, vec), min((u.n + kThreads - 1) / kThreads, (int64_t)1024));
   const int32_t ppr = d * elem_bytes / 16;
   const int64_t pieces = (int64_t)num_tokens * hkv * ppr;
   const int64_t g = up + grid_for(pieces);
@@ -503,12 +518,12 @@ int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slot
     upload_append_kernel<2><<<(unsigned)g, kThreads, 0, st>>>(
         (uint8_t*)dst, (const uint8_t*)src, bytes, vec, (int32_t)up, (const uint8_t*)k_new,
         (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, num_blocks, (uint8_t*)k_pool,
-        (uint8_t*)v_pool);
+        (uint8_t*)v_pool, u);
   else
     upload_append_kernel<4><<<(unsigned)g, kThreads, 0, st>>>(
         (uint8_t*)dst, (const uint8_t*)src, bytes, vec, (int32_t)up, (const uint8_t*)k_new,
         (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, num_blocks, (uint8_t*)k_pool,
-        (uint8_t*)v_pool);
+        (uint8_t*)v_pool, u);
   return status_of(hipGetLastError());
 }
 

@@ -2,7 +2,9 @@
 
 After a few timed steps of the GQA-4 workload at full size (64 sequences,
 ~150K context tokens), through the same function the benchmark times (host
-allocator step, upload of the index arrays fused with the append, decode):
+allocator step, upload of the index arrays and the changed table entries
+fused with the append, decode): the device-resident tables equal the host
+block manager's;
 the last step's output rows for sampled sequences match the oracle's decode
 over the pool the loop left behind, and the last step's new keys and values
 sit in their slots bit for bit.  Tolerance as for every bf16 decode: 2e-2
@@ -30,6 +32,9 @@ def test_decode_loop_output_and_appends(gpu):
     st = r["state"]
     torch.cuda.synchronize()
     assert len(r["durs"]) == args.steps and all(d > 0 for d in r["durs"])
+    # the device-resident tables, kept current by per-step last-entry
+    # updates, equal the host block manager's, bit for bit
+    assert np.array_equal(st["tables_dev"], st["tables"])
     kp, vp = words_of(st["k_pool"]), words_of(st["v_pool"])
     lens = st["lens"]
     tables = [row[:-(-int(L) // 16)].tolist() for row, L in zip(st["tables"], lens)]

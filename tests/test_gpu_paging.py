@@ -229,3 +229,45 @@ def test_upload_and_append_matches_separate_calls(gpu, n, dtype, d):
     kp, vp = words_of(k0).copy(), words_of(v0).copy()
     paging.append(kp, vp, kw, vw, slots, 16)
     assert np.array_equal(words_of(k1), kp) and np.array_equal(words_of(v1), vp)
+
+
+@pytest.mark.parametrize("n", [0, 64, 600])
+def test_upload_and_append_tables(gpu, n):
+    """upload_and_append_tables: the same upload and append as
+    upload_and_append, plus (index, value) pairs stored after the staged words
+    written into a device-resident table in the same launch (from 512 tokens
+    in the upload launch before the bulk append), bit for bit; indexes
+    outside the table are skipped, and the table's other words keep their
+    contents."""
+    hkv, d, nb, dtype = 4, 128, 96, "bf16"
+    rng = np.random.default_rng(910 + n)
+    slots = rng.permutation(nb * 16)[:n].astype(np.int32)
+    head = rng.integers(0, 1000, 12).astype(np.int32)
+    S, maxb = 37, 23
+    table0 = rng.integers(-1, nb, (S, maxb)).astype(np.int32)
+    idx = np.concatenate([rng.choice(S * maxb, 50, replace=False),
+                          [-1, S * maxb, S * maxb + 7]]).astype(np.int32)   # the last 3 are outside
+    val = rng.integers(0, nb, len(idx)).astype(np.int32)
+    pairs = np.stack([idx, val], 1).reshape(-1)
+    staging = torch.from_numpy(np.concatenate([head, slots, pairs])).pin_memory()
+    kw = normal_words(rng, (n, hkv, d), dtype)
+    vw = normal_words(rng, (n, hkv, d), dtype)
+    kn, vn = to_dev(kw, dtype), to_dev(vw, dtype)
+    k1, v1 = poisoned_pools(nb, hkv, d, dtype)
+    staged = len(head) + n
+    dst = torch.full((staged + 3,), -7, dtype=torch.int32, device="cuda")
+    tables = torch.from_numpy(table0).to("cuda")
+    _lib.upload_and_append(dst[:staged], staging, kn, vn, k1, v1, slots_at=len(head),
+                           tables=tables, num_updates=len(idx))
+    torch.cuda.synchronize()
+    want = table0.reshape(-1).copy()
+    inside = (idx >= 0) & (idx < S * maxb)
+    want[idx[inside]] = val[inside]
+    assert np.array_equal(tables.cpu().numpy().reshape(-1), want)
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:staged], np.concatenate([head, slots]))
+    assert (got[staged:] == -7).all()
+    k0, v0 = poisoned_pools(nb, hkv, d, dtype)
+    kp, vp = words_of(k0).copy(), words_of(v0).copy()
+    paging.append(kp, vp, kw, vw, slots, 16)
+    assert np.array_equal(words_of(k1), kp) and np.array_equal(words_of(v1), vp)

@@ -101,6 +101,14 @@ def test_bad_arguments_rejected(lib):
                                  None) == -1
     assert lib.upload_and_append(one, one, 64, 60, one, one, 4, one, one, 10, 8, 128, 16, 1,
                                  None) == -1 and b"staged" in lib.paged_kv_last_error()
+    # upload + append + table updates: negative count, updates without a
+    # table or after a staged size that is not a multiple of 4
+    f = lib.upload_and_append_tables
+    assert f(one, one, 64, 0, one, 100, -1, one, one, 4, one, one, 10, 8, 128, 16, 1, None) == -1
+    assert f(one, one, 64, 0, null, 100, 3, one, one, 4, one, one, 10, 8, 128, 16, 1,
+             None) == -1 and b"block_tables" in lib.paged_kv_last_error()
+    assert f(one, one, 62, 0, one, 100, 3, one, one, 4, one, one, 10, 8, 128, 16, 1, None) == -1
+    assert f(one, one, 64, 0, one, -5, 3, one, one, 4, one, one, 10, 8, 128, 16, 1, None) == -1
     # upload: negative size, null pointer
     assert lib.pinned_upload(one, one, -1, None) == -1
     assert lib.pinned_upload(null, one, 16, None) == -1 and b"null" in lib.paged_kv_last_error()
@@ -113,6 +121,8 @@ def test_empty_calls_are_no_ops(lib):
     assert lib.pinned_upload(null, null, 0, None) == 0
     assert lib.upload_and_append(null, null, 0, 0, null, null, 0, null, null, 10, 8, 128, 16, 1,
                                  None) == 0
+    assert lib.upload_and_append_tables(null, null, 0, 0, null, 0, 0, null, null, 0, null, null,
+                                        10, 8, 128, 16, 1, None) == 0
     assert lib.paged_kv_last_error() == b""
 
 
