@@ -232,15 +232,16 @@ def test_upload_and_append_matches_separate_calls(gpu, n, dtype, d):
 
 
 @pytest.mark.parametrize("n", [0, 64, 600])
-def test_upload_and_append_tables(gpu, n):
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_upload_and_append_tables(gpu, n, dtype, d):
     """upload_and_append_tables: the same upload and append as
     upload_and_append, plus (index, value) pairs stored after the staged words
     written into a device-resident table in the same launch (from 512 tokens
     in the upload launch before the bulk append), bit for bit; indexes
     outside the table are skipped, and the table's other words keep their
     contents."""
-    hkv, d, nb, dtype = 4, 128, 96, "bf16"
-    rng = np.random.default_rng(910 + n)
+    hkv, nb = 4, 96
+    rng = np.random.default_rng(910 + n + d)
     slots = rng.permutation(nb * 16)[:n].astype(np.int32)
     head = rng.integers(0, 1000, 12).astype(np.int32)
     S, maxb = 37, 23
