@@ -64,6 +64,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (counter calibration)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the device-copy bandwidth ceiling measurement")
+    ap.add_argument("--flush-iters", type=int, default=50,
+                    help="separate timing pass: this many calls of the dominant kernel on the "
+                         "last step's inputs, each after a 1 GiB scratch write that evicts the "
+                         "L2 and MALL caches, each bracketed by HIP events (0 = skip)")
     return ap.parse_args()
 
 
@@ -116,7 +122,11 @@ def cpu_baseline(case, seconds):
     for i, t in enumerate(tabs):
         tab[i, :len(t)] = t
     _CPU.update(q=case.q, kp=kp, vp=vp, tab=tab, lens=case.context_lens, scale=case.scale)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    # one worker per core this process may run on, at most 16: the host share
+    # a single GPU's job gets on the measurement machines, whatever the
+    # affinity mask shows
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, affinity))
     S = case.num_seqs
     chunks = [list(range(i, S, cores)) for i in range(cores)]
     ctx = mp.get_context("fork")
@@ -132,7 +142,8 @@ def cpu_baseline(case, seconds):
     _CPU.clear()
     tok_s = steps * S / el
     kv_bytes = float(np.sum(case.context_lens)) * 2 * case.num_kv_heads * case.head_dim * 2
-    return {"value": round(tok_s, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": round(tok_s, 3), "unit": "tokens/s", "cores": cores,
+            "affinity_cores": affinity, "kind": "oracle",
             "sample": f"{steps} full decode step(s) of the same workload ({S} sequences x "
                       f"{case.num_q_heads} heads, {int(np.sum(case.context_lens))} context "
                       f"tokens), {el:.1f} s on {cores} processes x 1 BLAS thread",
@@ -164,6 +175,49 @@ def load_traffic(workload, files):
 
 
 # ---------------------------------------------------------------- GPU steps
+def flushed_times(torch, call, iters):
+    """Durations in seconds of ``call()`` (kernels on torch's current stream,
+    the stream the library launches on), each call preceded by a 1 GiB
+    scratch write that evicts the L2 caches and the MALL, and bracketed by
+    HIP events on that stream (the write is outside the events)."""
+    if iters <= 0:
+        return []
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    pairs = []
+    for i in range(iters):
+        scratch.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    del scratch
+    return [a.elapsed_time(b) * 1e-3 for a, b in pairs]
+
+
+def bandwidth_ceilings(torch, lib, iters=10):
+    """Measured HBM ceilings, GB/s, each the median of ``iters`` calls with
+    the caches flushed before each: the library's read probe over a 2 GiB
+    buffer in a random order of 4 KB chunks (the scatter a paged pool's
+    (block, KV head) slabs have) and in address order, and a 2 GiB
+    device-to-device copy (torch copy_; read + written bytes)."""
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    order = torch.from_numpy(np.random.default_rng(0).permutation(n // 4096).astype(np.int32)).cuda()
+    sink = torch.zeros(8 * torch.cuda.get_device_properties(0).multi_processor_count,
+                       dtype=torch.int32, device="cuda")
+    rnd = flushed_times(torch, lambda: lib.hbm_read_probe(a, 4096, order, sink), iters)
+    seq = flushed_times(torch, lambda: lib.hbm_read_probe(a, 4096, None, sink), iters)
+    b = torch.empty_like(a)
+    cpy = flushed_times(torch, lambda: b.copy_(a), iters)
+    del a, b
+    return {"read_random_4k_gbps": round(n / float(np.median(rnd)) / 1e9, 1),
+            "read_sequential_gbps": round(n / float(np.median(seq)) / 1e9, 1),
+            "copy_gbps": round(2 * n / float(np.median(cpy)) / 1e9, 1)}
+
+
 def run_decode(args, case, torch, lib, alloc_cls):
     """Decode loop over a plain (unshared) decode case."""
     dev = torch.device("cuda:0")
@@ -241,21 +295,35 @@ def run_decode(args, case, torch, lib, alloc_cls):
         if sample:
             e1.record()
             ev_pairs.append((e0, e1))
+            lens_sampled.append(alloc.lens[:S].copy())
+        if timed:
             lens_seen.append(alloc.lens[:S].copy())     # bytes are counted after timing
+        return mcl
 
+    lens_sampled = []
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, T):
-        step(i, True)
+        mcl = step(i, True)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
-    step_bytes = [int(ln.sum()) * kv_per_tok + 2 * S * hq * d * 2 + int((-(-ln // 16)).sum()) * 4
-                  + S * 4 for ln in lens_seen]
+
+    def call_bytes(ln):
+        return (int(ln.sum()) * kv_per_tok + 2 * S * hq * d * 2 + int((-(-ln // 16)).sum()) * 4
+                + S * 4)
+
+    # the last step's decode call again, caches flushed before each
+    flush = flushed_times(torch, lambda: lib.paged_attention_decode(
+        out, q_steps[T - 1], k_pool, v_pool, tables_d, lens_d, mcl, case.scale,
+        args.partition_size, ws), args.flush_iters)
     alloc.validate()
-    res = dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=step_bytes,
+    res = dict(elapsed=el, tokens=S * args.steps, durs=durs,
+               bytes=[call_bytes(ln) for ln in lens_sampled],
+               step_bytes=[call_bytes(ln) for ln in lens_seen],
+               flush_durs=flush, flush_bytes=call_bytes(lens_seen[-1]),
                ctx_mean=float(alloc.lens[:S].mean()))
     if getattr(args, "keep_state", False):     # for tests of this loop: what the last step saw
         res["state"] = dict(out=out, q=q_steps[T - 1], k_new=k_steps[T - 1], v_new=v_steps[T - 1],
@@ -329,7 +397,19 @@ def run_extend(args, case, torch, lib, alloc_cls):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
-    res = dict(elapsed=el, tokens=n_new * args.steps, durs=durs, flops=flops)
+    # one more chunk in place, then the extend call again with caches flushed
+    # before each call
+    sl = np.concatenate([alloc.append_tokens(s, int(n))[0] for s, n in zip(sids, case.new_lens)])
+    buf = ring[0].numpy()
+    ring_ev[0].synchronize()
+    buf[:n_new] = sl
+    buf[n_new:] = alloc.tables[:R].reshape(-1)
+    lib.upload_and_append(stage, ring[0], k_new, v_new, k_pool, v_pool)
+    torch.cuda.synchronize()
+    flush = flushed_times(torch, lambda: lib.paged_attention_extend(
+        out, q, cu, seq_lens, k_pool, v_pool, tables_d, int(case.new_lens.max()),
+        int(case.seq_lens.max()), case.scale), args.flush_iters)
+    res = dict(elapsed=el, tokens=n_new * args.steps, durs=durs, flops=flops, flush_durs=flush)
     if getattr(args, "keep_state", False):     # for tests of this loop: what the last step saw
         res["state"] = dict(out=out, k_pool=k_pool, v_pool=v_pool,
                             tables=tables_d.cpu().numpy().copy())
@@ -437,6 +517,15 @@ def run_shared(args, case, torch, lib, alloc_cls):
             snaps.append((alloc.tables[rows].copy(), lens.copy()))
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    # the last step's decode call again, caches flushed before each call
+    if groups is None:
+        again = lambda: lib.paged_attention_decode(out, q_steps[T - 1], k_pool, v_pool, tables_d,
+                                                   lens_d, int(lens.max()), case.scale, 0, ws)
+    else:
+        again = lambda: lib.paged_attention_decode_shared(out, q_steps[T - 1], k_pool, v_pool,
+                                                          tables_d, lens_d, maxb * 16, case.scale,
+                                                          groups, 0, ws)
+    flush = flushed_times(torch, again, args.flush_iters)
     uniq, logical = [], []
     for tabs, lens in snaps:        # distinct (block, used slot) pairs, counted once
         used = {}
@@ -448,8 +537,9 @@ def run_shared(args, case, torch, lib, alloc_cls):
         uniq.append(sum(used.values()) * kv_per_tok)
         logical.append(int(lens.sum()) * kv_per_tok)
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
-    return dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=uniq, logical=logical,
-                cow_pairs=n_pairs, shared=groups is not None)
+    return dict(elapsed=el, tokens=S * args.steps, durs=durs, bytes=uniq, step_bytes=uniq,
+                logical=logical, cow_pairs=n_pairs, shared=groups is not None,
+                flush_durs=flush, flush_bytes=uniq[-1], flush_logical=logical[-1])
 
 
 def run_swap(args, case, torch, lib, alloc_cls):
@@ -699,26 +789,45 @@ def main():
 
     el = r["elapsed"]
     ms_step = el / args.steps * 1e3
-    mean_dur = float(np.mean(r["durs"]))
     traffic, _ = load_traffic(args.workload, kern)
+    # Launch time of the dominant call: the median of the flushed timing pass
+    # (caches evicted before every call); without that pass, the mean of the
+    # step loop's sampled events.
+    flush = r.get("flush_durs") or []
+    warm = float(np.mean(r["durs"]))
+    t_call = float(np.median(flush)) if flush else warm
+    timing = {"launch_us": round(t_call * 1e6, 2),
+              "launch_us_is": ("median of %d calls, L2/MALL flushed by a 1 GiB write before each"
+                               % len(flush)) if flush else
+                              "mean of the step loop's sampled calls (no flush)",
+              "launch_us_min": round(float(np.min(flush)) * 1e6, 2) if flush else None,
+              "launch_us_mean_flushed": round(float(np.mean(flush)) * 1e6, 2) if flush else None,
+              "launch_us_mean_in_step_loop": round(warm * 1e6, 2)}
     if args.workload == "multiturn-extend":
-        achieved = r["flops"] / mean_dur / 1e12
+        achieved = r["flops"] / t_call / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": "paged_attention_extend (extend_bf16_kernel)",
-                "launch_us": round(mean_dur * 1e6, 2), "flops_per_launch": r["flops"]}
+                **timing, "flops_per_launch": r["flops"]}
         value = r["tokens"] / el
         unit = "tokens/s"
         metric = "paged extend bf16 matrix-core TFLOP/s and new tokens/s (multi-turn prefill)"
     else:
-        per_launch = float(np.mean(r["bytes"]))
-        achieved = per_launch / mean_dur / 1e9
+        per_launch = float(r["flush_bytes"]) if flush else float(np.mean(r["bytes"]))
+        achieved = per_launch / t_call / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": ("paged_attention_decode_shared (prefix pass extend_bf16_kernel<PREFIX> "
-                           "+ decode_bf16_kernel<SHARED>)" if r.get("shared") else
-                           "paged_attention_decode (decode_bf16_kernel, merge fused)"),
-                "launch_us": round(mean_dur * 1e6, 2), "bytes_per_launch": int(per_launch)}
+                           "+ decode_bf16_kernel<SHARED> + decode_fold_kernel)" if r.get("shared")
+                           else "paged_attention_decode (decode_bf16_kernel, merge fused)"),
+                **timing, "bytes_per_launch": int(per_launch)}
+        if not args.no_ceiling:
+            ceil = bandwidth_ceilings(torch, lib)
+            ceil["frac_of_read_random_4k"] = round(achieved / ceil["read_random_4k_gbps"], 4)
+            ceil["note"] = ("medians of 10 flushed calls: hbm_read_probe over a 2 GiB buffer in a "
+                            "random order of 4 KB chunks and in address order; torch copy_ of "
+                            "2 GiB counts read + written bytes")
+            roof["ceiling"] = ceil
         value = r["tokens"] / el
         unit = "tokens/s"
         metric = METRIC
@@ -745,9 +854,12 @@ def main():
             "data": "synthetic (seeded N(0,1) bf16 K/V/Q, shuffled block placement)",
             "config": cfg, "roofline": roof, "cpu_baseline": cpu}
     if args.workload != "multiturn-extend":
-        line["step_hbm_gbps"] = round(float(np.sum(r["bytes"])) / el / 1e9, 1)
+        # algorithmic bytes of every timed step's decode call over the wall
+        # time of all timed steps (the whole step, not just the decode call)
+        line["step_hbm_gbps"] = round(float(np.sum(r["step_bytes"])) / el / 1e9, 1)
     if "logical" in r:
-        roof["logical_gbps_effective"] = round(float(np.mean(r["logical"])) / mean_dur / 1e9, 1)
+        lg = float(r["flush_logical"]) if flush else float(np.mean(r["logical"]))
+        roof["logical_gbps_effective"] = round(lg / t_call / 1e9, 1)
         line["cow_pairs_in_run"] = r["cow_pairs"]
     print(json.dumps(line), flush=True)
 

@@ -118,9 +118,10 @@ int copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks,
  * Talk About KV Cache", section "Beyond the Two Techniques", hierarchical
  * memory: hot blocks in GPU memory, recently used ones in host RAM).
  *
- *   dst_k, dst_v   [dst_num_blocks][num_kv_heads][block_size][head_dim] pools
- *                  (the pool layout of paged_kv_append), written
- *   src_k, src_v   [src_num_blocks][...] pools, read
+ *   dst_k, dst_v   pools of dst_num_blocks blocks in the layout above (K
+ *                  [..][num_kv_heads][block_size][head_dim], V
+ *                  [..][num_kv_heads][head_dim][block_size]), written
+ *   src_k, src_v   pools of src_num_blocks blocks, same layout, read
  *   block_mapping  [num_pairs][2] int32, device memory: (src block, dst block)
  *
  * Each pool is device memory or pinned host memory (hipHostMalloc, or a
@@ -482,6 +483,24 @@ int block_manager_append_step(int32_t* tables, int32_t* lens, int32_t* nblk,
                               int32_t num_blocks, int32_t block_size, const int64_t* sids,
                               int32_t num_sids, int32_t* free_ring, int64_t* free_state,
                               int32_t* slots_out, int32_t* pairs_out, int32_t* num_pairs_out);
+
+/*
+ * hbm_read_probe -- measurement support, not a step of the method: reads
+ * num_chunks chunks of chunk_bytes bytes from buf with non-temporal 16-byte
+ * loads, in the order chunk_order gives (num_chunks int32 entries in
+ * [0, num_chunks), device memory; NULL = address order), and folds what it
+ * read into sink[0 .. num_workgroups-1] (device uint32 words, XORed into).
+ * The buffer holds num_chunks * chunk_bytes bytes.  Timing it over a random
+ * order of 4 KB chunks gives the practical rate of the scattered 4 KB reads
+ * a paged pool makes (a bf16 (block, KV head) slab at head_dim 128 is 4 KB),
+ * the ceiling the decode kernels' bandwidth is reported against beside the
+ * HBM peak.  Out-of-range order entries read chunk 0.  PKV_ERR_INVALID for
+ * null pointers, negative counts or sizes and pointers that are not
+ * multiples of 16 bytes.
+ */
+int hbm_read_probe(const void* buf, int64_t num_chunks, int32_t chunk_bytes,
+                   const int32_t* chunk_order, uint32_t* sink, int32_t num_workgroups,
+                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ SYMBOLS = ("paged_kv_append", "copy_blocks", "swap_blocks", "paged_attention_dec
            "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
            "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
            "paged_kv_last_error", "block_manager_append_step", "pinned_upload",
-           "upload_and_append", "upload_and_append_tables")
+           "upload_and_append", "upload_and_append_tables", "hbm_read_probe")
 
 
 class PagedKVError(RuntimeError):
@@ -73,6 +73,8 @@ def load():
     lib.upload_and_append_tables.argtypes = [p, p, ctypes.c_int64, ctypes.c_int64, p,
                                              ctypes.c_int64, i32, p, p, i32, p, p, i32, i32, i32,
                                              i32, i32, p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    lib.hbm_read_probe.argtypes = [p, ctypes.c_int64, i32, p, p, i32, p]
     lib.block_manager_append_step.restype = ctypes.c_int
     lib.block_manager_append_step.argtypes = [p, p, p, p, p, i32, i32, p, p, i32, i32, p, i32,
                                               p, p, p, p, p]
@@ -369,6 +371,30 @@ def paged_attention_extend(out, q, cu_seqlens_q, seq_lens, k_pool, v_pool, block
                                          _ptr(v_pool), nb, _ptr(block_tables),
                                          block_tables.shape[1], hq, hkv, d, bs, float(scale), dt,
                                          _stream()))
+
+
+def hbm_read_probe(buf, chunk_bytes, chunk_order=None, sink=None, num_workgroups=None):
+    """Read the device buffer ``buf`` once in chunks of ``chunk_bytes`` bytes
+    (in the order of the int32 device tensor ``chunk_order``, or in address
+    order) -- the measured ceiling for scattered block reads.  Returns the
+    sink tensor the reads are folded into."""
+    _dev(buf)
+    nbytes = buf.numel() * buf.element_size()
+    if nbytes % chunk_bytes:
+        raise ValueError("the buffer must hold a whole number of chunks")
+    n = nbytes // chunk_bytes
+    if chunk_order is not None:
+        _dev(chunk_order)
+        _int32(chunk_order)
+        if chunk_order.numel() != n:
+            raise ValueError("chunk_order must list every chunk once")
+    if num_workgroups is None:
+        num_workgroups = 8 * torch.cuda.get_device_properties(buf.device).multi_processor_count
+    if sink is None:
+        sink = torch.zeros(num_workgroups, dtype=torch.int32, device=buf.device)
+    _check(load().hbm_read_probe(_ptr(buf), n, int(chunk_bytes), _ptr(chunk_order), _ptr(sink),
+                                 int(num_workgroups), _stream()))
+    return sink
 
 
 def paged_kv_gather(k_out, v_out, k_pool, v_pool, block_table_row, context_len):

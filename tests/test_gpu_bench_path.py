@@ -25,13 +25,14 @@ pytestmark = pytest.mark.gpu
 
 
 def test_decode_loop_output_and_appends(gpu):
-    args = argparse.Namespace(warmup=2, steps=3, partition_size=0, event_every=1,
+    args = argparse.Namespace(warmup=2, steps=3, partition_size=0, event_every=1, flush_iters=2,
                               keep_state=True)
     case = bench.make_case("gqa4-decode", args.warmup + args.steps)
     r = bench.run_decode(args, case, torch, _lib, BlockAllocator)
     st = r["state"]
     torch.cuda.synchronize()
     assert len(r["durs"]) == args.steps and all(d > 0 for d in r["durs"])
+    assert len(r["flush_durs"]) == 2 and min(r["flush_durs"]) > 0
     # the device-resident tables, kept current by per-step last-entry
     # updates, equal the host block manager's, bit for bit
     assert np.array_equal(st["tables_dev"], st["tables"])
@@ -55,7 +56,7 @@ def test_extend_loop_output(gpu):
     """The multi-turn extend loop (16 requests, 2K-8K cached tokens + 512 new
     each): the last step's output for 2 requests x 2 query heads against the
     oracle over the pool and tables that step used."""
-    args = argparse.Namespace(warmup=1, steps=2, keep_state=True)
+    args = argparse.Namespace(warmup=1, steps=2, keep_state=True, flush_iters=2)
     e = bench.make_case("multiturn-extend", args.warmup + args.steps)
     r = bench.run_extend(args, e, torch, _lib, BlockAllocator)
     st = r["state"]

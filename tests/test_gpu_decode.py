@@ -58,10 +58,13 @@ def test_gqa4_full_size(gpu):
     assert err <= 2e-2, err
 
 
-def test_long_context_full_size_sampled(gpu):
+@pytest.mark.timeout(600)
+def test_long_context_full_size(gpu):
     """Llama-3.1-70B shape, 8 sequences of 32K..128K tokens, 512-token
-    partitions; the oracle checks two sequences x two KV heads (all their
-    query heads) and, for every sequence, the all-heads output is finite."""
+    pieces: every output (8 sequences x 64 query heads) against the oracle.
+    The oracle runs per (sequence, KV head) over the gathered keys and values
+    of that head, the units spread over host threads."""
+    from concurrent.futures import ThreadPoolExecutor
     case = long_context_decode()
     st = LibDecodeState(case)
     out, _ = st.decode(partition_size=512)
@@ -70,15 +73,22 @@ def test_long_context_full_size_sampled(gpu):
     kp, vp, tab = P.oracle_pools_for_decode(case)
     g = case.num_q_heads // case.num_kv_heads
     q = numerics.to_f64(case.q, "bf16")
-    for s in (int(np.argmax(case.context_lens)), int(np.argmin(case.context_lens))):
+
+    def one_seq(s):
         L = int(case.context_lens[s])
         kw, vw = paging.gather_fast(kp, vp, tab[s], L, 16)
-        for h in (0, case.num_kv_heads - 1):
+        worst = 0.0
+        for h in range(case.num_kv_heads):
             k = numerics.to_f64(kw[:, h:h + 1], "bf16")
             v = numerics.to_f64(vw[:, h:h + 1], "bf16")
             want = attention.attend(q[s, h * g:(h + 1) * g], k, v, case.scale)
-            err = np.abs(got[s, h * g:(h + 1) * g] - want).max()
-            assert err <= 2e-2, (s, h, err)
+            worst = max(worst, float(np.abs(got[s, h * g:(h + 1) * g] - want).max()))
+        return worst
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        errs = list(ex.map(one_seq, range(case.num_seqs)))
+    print("long-context decode max |err| per sequence:", ["%.2e" % e for e in errs])
+    assert max(errs) <= 2e-2, errs
 
 
 def decode_plan(lens, hkv, piece_tokens, workgroups):
