@@ -224,6 +224,36 @@ int paged_attention_decode(void* out, const void* q,
                            int32_t dtype, void* stream);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
+ * result as paged_attention_decode, without the workspace arguments: the
+ * call's pieces and arrival words live in a fixed array the library holds
+ * on every GPU it runs on (64 MiB, kept until the process ends).  The call
+ * allocates nothing.
+ *
+ * Limits: num_seqs * num_kv_heads <= 32768, and the partials,
+ * num_seqs * num_q_heads * P * (head_dim + 2) * 4 bytes with P as in
+ * paged_attention_decode, at most 64 MiB - 256 KiB (a larger partition_size
+ * lowers P).  Beyond them the call returns PKV_ERR_WORKSPACE, with both
+ * sizes in the message, and enqueues nothing.
+ *
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls in order on one stream are fine, but calls that overlap in
+ * time on one GPU (other streams, other host threads) race and give wrong
+ * results.  The first call on a GPU also enqueues, on `stream`, a small
+ * kernel that clears the array's arrival words.
+ */
+int paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                   const void* v_pool, int32_t num_blocks,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t max_context_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   float scale, int32_t partition_size, int32_t dtype,
+                                   void* stream);
+
+/*
  * Size in bytes of the workspace paged_attention_decode_shared needs for
  * these arguments (it depends on the device's compute-unit count, which
  * sets the prefix pass's key split).  Returns 0 for invalid arguments.

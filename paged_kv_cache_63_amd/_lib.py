@@ -23,7 +23,8 @@ SYMBOLS = ("paged_kv_append", "copy_blocks", "swap_blocks", "paged_attention_dec
            "paged_attention_decode", "paged_attention_decode_shared_workspace_size",
            "paged_attention_decode_shared", "paged_attention_extend", "paged_kv_gather",
            "paged_kv_last_error", "block_manager_append_step", "pinned_upload",
-           "upload_and_append", "upload_and_append_tables", "hbm_read_probe")
+           "upload_and_append", "upload_and_append_tables", "hbm_read_probe",
+           "paged_attention_decode_noalloc")
 
 
 class PagedKVError(RuntimeError):
@@ -53,6 +54,9 @@ def load():
     lib.paged_attention_decode.restype = ctypes.c_int
     lib.paged_attention_decode.argtypes = [p, p, p, p, i32, p, i32, p, i32, i32, i32, i32, i32,
                                            i32, f32, i32, p, sz, i32, p]
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc.argtypes = [p, p, p, p, i32, p, i32, p, i32, i32, i32, i32,
+                                                   i32, i32, f32, i32, i32, p]
     lib.paged_attention_decode_shared_workspace_size.restype = sz
     lib.paged_attention_decode_shared_workspace_size.argtypes = [i32] * 9
     lib.paged_attention_decode_shared.restype = ctypes.c_int
@@ -272,6 +276,24 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
                                          bs, float(scale), int(partition_size), _ptr(workspace),
                                          wbytes, dt, _stream()))
     return workspace
+
+
+def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens,
+                                   max_context_len, scale, partition_size=0):
+    """paged_attention_decode with the library's fixed per-GPU workspace
+    (nothing is allocated, here or in the library)."""
+    nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
+    _dev(out, q, k_pool, v_pool, block_tables, context_lens)
+    _int32(block_tables, context_lens)
+    S, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (S, hq, d) or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("q/out must be [S][Hq][D] in the pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables [S][max_blocks], context_lens [S]")
+    _check(load().paged_attention_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), S, int(max_context_len), hq, hkv, d, bs,
+        float(scale), int(partition_size), dt, _stream()))
 
 
 def paged_attention_decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,

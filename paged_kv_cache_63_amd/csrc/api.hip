@@ -307,13 +307,16 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
          (size_t)num_seqs * num_kv_heads * sizeof(uint64_t);
 }
 
-int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                           int32_t num_blocks, const int32_t* block_tables,
-                           int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                           int32_t partition_size, void* workspace, size_t workspace_bytes,
-                           int32_t dtype, void* stream) {
+namespace {
+
+// Checks shared by the decode entries; sets *P (pieces per context the
+// partials hold) and *ptok (piece tokens) on success.
+int decode_prepare(const void* out, const void* q, const void* k_pool, const void* v_pool,
+                   int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t partition_size, int32_t dtype, int64_t* P,
+                   int32_t* ptok) {
   int rc = check_common(num_kv_heads, head_dim, block_size, dtype);
   if (rc) return rc;
   rc = check_heads(num_q_heads, num_kv_heads);
@@ -324,26 +327,28 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID, "null pointer argument");
   if ((int64_t)num_seqs * num_kv_heads > INT32_MAX) return fail(PKV_ERR_INVALID, "too many sequences");
-  const int32_t ptok = choose_piece(partition_size);
-  if (ptok < 0 || ptok % block_size)
+  *ptok = choose_piece(partition_size);
+  if (*ptok < 0 || *ptok % block_size)
     return fail(PKV_ERR_INVALID, "partition_size %d must be a multiple of %d", partition_size,
                 block_size);
-  const int64_t P = max_pieces(max_context_len, ptok);
-  if (P > kMaxPieces || (dtype == 0 && P - 1 > 65535))
+  *P = max_pieces(max_context_len, *ptok);
+  if (*P > kMaxPieces || (dtype == 0 && *P - 1 > 65535))
     return fail(PKV_ERR_INVALID, "max_context_len %d needs %lld pieces per context (too many)",
-                max_context_len, (long long)P);
+                max_context_len, (long long)*P);
   // a merge stages [2][group][P] + [group] fp32 weights in LDS (160 KB)
-  if (dtype == 1 && (2 * (num_q_heads / num_kv_heads) * P + 16) * 4 > 160 * 1024 - 256)
+  if (dtype == 1 && (2 * (num_q_heads / num_kv_heads) * *P + 16) * 4 > 160 * 1024 - 256)
     return fail(PKV_ERR_UNSUPPORTED,
                 "max_context_len %d over partition_size %d gives %lld pieces per context; use a "
-                "larger partition_size", max_context_len, ptok, (long long)P);
-  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
-                                                            head_dim, max_context_len, ptok);
-  if (!workspace || workspace_bytes < need)
-    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  if ((uintptr_t)workspace % 8)
-    return fail(PKV_ERR_WORKSPACE, "workspace must be 8-byte aligned");
+                "larger partition_size", max_context_len, *ptok, (long long)*P);
+  return PKV_OK;
+}
 
+pkv::DecodeArgs decode_args(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            int32_t num_blocks, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, float scale, int32_t ptok,
+                            int64_t P, float* part_o, uint64_t* arrive) {
   pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -351,16 +356,12 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  {
-    float* ws = (float*)workspace;
-    const int64_t rows = (int64_t)num_seqs * num_q_heads * P;
-    a.part_o = ws;
-    a.part_m = ws + rows * head_dim;
-    a.part_l = a.part_m + rows;
-    // rows * (D + 2) floats: a multiple of 8 bytes, so the words are aligned
-    a.arrive = (uint64_t*)(a.part_l + rows);
-    a.tag = next_call_tag();
-  }
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * P;
+  a.part_o = part_o;
+  a.part_m = part_o + rows * head_dim;
+  a.part_l = a.part_m + rows;
+  a.arrive = arrive;
+  a.tag = next_call_tag();
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -371,6 +372,75 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   a.max_partitions = (int32_t)P;
   a.num_workgroups = decode_workgroups();
   a.scale = scale;
+  return a;
+}
+
+}  // namespace
+
+int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           int32_t num_blocks, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           int32_t dtype, void* stream) {
+  int64_t P = 0;
+  int32_t ptok = 0;
+  int rc = decode_prepare(out, q, k_pool, v_pool, num_blocks, block_tables, max_blocks_per_seq,
+                          context_lens, num_seqs, max_context_len, num_q_heads, num_kv_heads,
+                          head_dim, block_size, partition_size, dtype, &P, &ptok);
+  if (rc || num_seqs == 0) return rc;
+  const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                            head_dim, max_context_len, ptok);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if ((uintptr_t)workspace % 8)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 8-byte aligned");
+  float* ws = (float*)workspace;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * P;
+  // rows * (D + 2) floats: a multiple of 8 bytes, so the words are aligned
+  uint64_t* arrive = (uint64_t*)(ws + rows * (head_dim + 2));
+  const pkv::DecodeArgs a =
+      decode_args(out, q, k_pool, v_pool, num_blocks, block_tables, max_blocks_per_seq,
+                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                  ptok, P, ws, arrive);
+  rc = pkv::launch_decode(a, dtype, (hipStream_t)stream);
+  return rc ? fail(rc, "decode launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();
+}
+
+int paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                   const void* v_pool, int32_t num_blocks,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t max_context_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   float scale, int32_t partition_size, int32_t dtype,
+                                   void* stream) {
+  int64_t P = 0;
+  int32_t ptok = 0;
+  int rc = decode_prepare(out, q, k_pool, v_pool, num_blocks, block_tables, max_blocks_per_seq,
+                          context_lens, num_seqs, max_context_len, num_q_heads, num_kv_heads,
+                          head_dim, block_size, partition_size, dtype, &P, &ptok);
+  if (rc || num_seqs == 0) return rc;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int64_t part_bytes = (int64_t)num_seqs * num_q_heads * P * (head_dim + 2) * 4;
+  constexpr int64_t kMaxUnits = (int64_t)(pkv::kScratchArriveBytes / 8);
+  constexpr int64_t kPartMax = (int64_t)(pkv::kScratchBytes - pkv::kScratchArriveBytes);
+  if (units > kMaxUnits || part_bytes > kPartMax)
+    return fail(PKV_ERR_WORKSPACE,
+                "the allocation-free decode's fixed workspace is too small: %lld (sequence, KV "
+                "head) units (at most %lld) and %lld bytes of partials (at most %lld); a larger "
+                "partition_size or fewer sequences per call fit, or use paged_attention_decode",
+                (long long)units, (long long)kMaxUnits, (long long)part_bytes,
+                (long long)kPartMax);
+  uint8_t* base = nullptr;
+  rc = pkv::decode_scratch((hipStream_t)stream, &base);
+  if (rc) return fail(rc, "allocation-free decode: no workspace on this device (%s)",
+                      hipGetErrorString(hipGetLastError()));
+  const pkv::DecodeArgs a =
+      decode_args(out, q, k_pool, v_pool, num_blocks, block_tables, max_blocks_per_seq,
+                  context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                  ptok, P, (float*)(base + pkv::kScratchArriveBytes), (uint64_t*)base);
   rc = pkv::launch_decode(a, dtype, (hipStream_t)stream);
   return rc ? fail(rc, "decode launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();
 }

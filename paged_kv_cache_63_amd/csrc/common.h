@@ -113,6 +113,17 @@ struct DecodeArgs {
 
 int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st);
 
+// The decode workspace the allocation-free entry uses: one fixed device
+// array per GPU, kScratchBytes long, whose first kScratchArriveBytes hold the
+// arrival words (one per (sequence, KV head), so at most
+// kScratchArriveBytes / 8 units) and the rest the pieces' partials.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchArriveBytes = size_t(256) << 10;
+// Device address of the current device's array; the first call on a device
+// looks it up and clears its arrival words with a kernel on st.  0 or a
+// PKV_ERR_* code.
+int decode_scratch(hipStream_t st, uint8_t** base);
+
 struct ExtendArgs {
   void* out;
   const void* q;

@@ -14,8 +14,15 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
+
+// Workspace of the allocation-free decode entry: a fixed array on every GPU
+// the library runs on, held until the process ends.  Host code never uses
+// this name as an address: the per-device address comes from
+// hipGetSymbolAddress (decode_scratch below).
+static __device__ __align__(256) uint8_t scratch[pkv::kScratchBytes];
 
 namespace pkv {
 namespace {
@@ -739,7 +746,33 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
   return status_of(e);
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(uint64_t* w, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    w[i] = 0;
+}
+
 }  // namespace
+
+int decode_scratch(hipStream_t st, uint8_t** base) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices];   // per device, set once
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -2;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -4;
+    // arrival words start at zero (no call's tag is zero); the partials need
+    // no initial value
+    constexpr int64_t words = (int64_t)(kScratchArriveBytes / 8);
+    zero_words_kernel<<<(unsigned)(words / 256 / 8), 256, 0, st>>>((uint64_t*)p, words);
+    if (hipGetLastError() != hipSuccess) return -4;
+    addr[dev] = (uint8_t*)p;
+  }
+  *base = addr[dev];
+  return 0;
+}
 
 int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
   if (a.num_seqs == 0) return 0;
