@@ -93,23 +93,29 @@ __device__ __forceinline__ void materialize(T& x) {
   asm volatile("" : "+v"(x));
 }
 
-// One direct-to-LDS copy: every lane loads 16 bytes from sbase + voff
-// (sbase wave-uniform) and the wave writes them to LDS at lds + lane*16.
-// Issued as inline assembly so that the compiler neither hoists 64-bit
-// per-lane addresses out of the loop nor adds waits for these copies
-// before unrelated LDS reads; the kernel waits for them itself (vmcnt).
-// M0 (the LDS base of the copy) is saved and restored around it; the
+// Two direct-to-LDS copies, the K and the V slab of one block: every lane
+// loads 16 bytes from kbase + koff (then vbase + voff), bases wave-uniform,
+// and the wave writes them to LDS at lds_k + lane*16 (then lds_v +
+// lane*16).  Issued as inline assembly so that the compiler neither hoists
+// 64-bit per-lane addresses out of the loop nor adds waits for these copies
+// before unrelated LDS reads; the kernel waits for them itself (vmcnt).  M0
+// (the LDS base of a copy) is saved once and restored after both; each
 // s_nop covers the M0-write hazard.
-__device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void lds_dma16_kv(const uint8_t* kbase, uint32_t koff,
+                                             const uint8_t* vbase, uint32_t voff, uint32_t lds_k,
+                                             uint32_t lds_v) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %5\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %4\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds)
+      : "v"(koff), "s"(kbase), "v"(voff), "s"(vbase), "s"(lds_k), "s"(lds_v)
       : "memory");
 }
 
@@ -270,56 +276,51 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
 
   const uint8_t* kpool = (const uint8_t*)a.k_pool;
   const uint8_t* vpool = (const uint8_t*)a.v_pool;
-  // Physical block of logical block kb (block 0 past the end of the
-  // sequence or for an invalid entry; such keys are masked where used).
-  // The table word is loaded well before its copy is issued and checked
-  // only then, so the scalar load's latency stays off the critical path.
-  auto entry_raw = [&](int kb) -> int { return trow[kb < nblk ? kb : 0]; };
-  auto entry_ok = [&](int kb, int e) -> int {
-    return (kb < nblk && e >= 0 && e < a.num_blocks) ? e : 0;
+  // Table word of logical block kb; past the end of the sequence, the
+  // sequence's last block (its keys there are masked where used).  The word
+  // is loaded well before its copy is issued and range-checked only then
+  // (an entry outside the pool reads block 0), so the scalar load's latency
+  // stays off the critical path.
+  auto entry_raw = [&](int kb) -> int { return trow[min(kb, nblk - 1)]; };
+  auto entry_ok = [&](int e) -> uint32_t {
+    return (uint32_t)e < (uint32_t)a.num_blocks ? (uint32_t)e : 0u;
   };
 
-  // Direct-to-LDS copy of tile t into stage st.  Load i of wave w fills the
-  // 64-chunk segment s = i*NW + w of the stage ([K tile | V tile]); which
-  // pool, which block of the tile and each lane's byte offset inside the
-  // head's slab are fixed per (i, w): computed once.
-  uint32_t src_off[PER_T];
-  int src_blk[PER_T];
-  bool src_v[PER_T];
+  // Direct-to-LDS copy of tile t into stage t % NST ([K tile | V tile]).
+  // Wave w copies, for each i < NBW, the 64-chunk segment s = i*NW + w of
+  // the K tile and the same segment of the V tile: both lie in block
+  // src_blk[i] of the tile, so each block's address is formed once.  Each
+  // lane's byte offsets inside the head's K and V slabs are fixed per
+  // (i, w): computed once.
+  constexpr int NBW = PER_T / 2;
+  static_assert(NBW * NW == SEGS, "a wave's K and V segments pair up block by block");
+  uint32_t src_off_k[NBW], src_off_v[NBW];
+  int src_blk[NBW];
 #pragma unroll
-  for (int i = 0; i < PER_T; ++i) {
-    const int s = i * NW + wave;
-    const int which = s / SEGS;
-    const int c0 = (s - which * SEGS) * kWave;   // first chunk of the segment in its tile
+  for (int i = 0; i < NBW; ++i) {
+    const int c0 = (i * NW + wave) * kWave;      // first chunk of the segment in its tile
     const int blk = c0 / (BLKB / 16);
     const int within = c0 - blk * (BLKB / 16) + lane;
-    int src_chunk;
-    if (which == 0) {
-      const int row = within / CPR;
-      const int pos = within - row * CPR;
-      src_chunk = row * CPR + (pos ^ ((row / SWZ) % CPR));
-    } else {
-      const int row = within >> 1;
-      src_chunk = within ^ (((row >> 2) ^ (row >> 3)) & 1);
-    }
-    src_off[i] = (uint32_t)(h * BLKB + src_chunk * 16);
+    const int row = within / CPR;
+    const int pos = within - row * CPR;
+    src_off_k[i] = (uint32_t)(h * BLKB + (row * CPR + (pos ^ ((row / SWZ) % CPR))) * 16);
+    const int vrow = within >> 1;
+    src_off_v[i] = (uint32_t)(h * BLKB + (within ^ (((vrow >> 2) ^ (vrow >> 3)) & 1)) * 16);
     src_blk[i] = blk;
-    src_v[i] = which != 0;
   }
-  const int64_t blk_stride = (int64_t)hkv * BLKB;   // bytes between physical blocks
-  auto fetch_entries = [&](int t, int (&e)[PER_T]) {
+  const uint32_t blk_stride = (uint32_t)(hkv * BLKB);   // bytes between physical blocks
+  auto fetch_entries = [&](int t, int (&e)[NBW]) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) e[i] = entry_raw((t + kt0) * NBT + src_blk[i]);
+    for (int i = 0; i < NBW; ++i) e[i] = entry_raw((t + kt0) * NBT + src_blk[i]);
   };
-  auto issue = [&](int t, const int (&e)[PER_T]) {
-    const int st = t % NST;
+  auto issue = [&](int t, const int (&e)[NBW]) {
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)(
+        &kv_s[t % NST][wave * kWave * 16]);
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int phys = entry_ok((t + kt0) * NBT + src_blk[i], e[i]);
-      const uint8_t* base = (src_v[i] ? vpool : kpool) + (int64_t)phys * blk_stride;
-      const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)(
-          &kv_s[st][(i * NW + wave) * kWave * 16]);
-      lds_dma16(base, src_off[i], lds);
+    for (int i = 0; i < NBW; ++i) {
+      const uint64_t off = (uint64_t)entry_ok(e[i]) * blk_stride;
+      const uint32_t lk = lds0 + i * NW * kWave * 16;
+      lds_dma16_kv(kpool + off, src_off_k[i], vpool + off, src_off_v[i], lk, lk + TILEB);
     }
   };
 
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     }
     wg_barrier();
   };
-  int e_nxt[PER_T];   // physical blocks of the next tile to copy
+  int e_nxt[NBW];   // table words of the next tile to copy
   auto copy_and_lookup = [&](int t) {
     if (t + 3 < ntiles) issue(t + 3, e_nxt);
     if (t + 4 < ntiles) fetch_entries(t + 4, e_nxt);
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
   const int nt = has_rows && wq_max >= kt0 * KT ? min(ntiles, (wq_max - kt0 * KT) / KT + 1) : 0;
   const int td = wq_min + 1 >= kt0 * KT ? (wq_min + 1 - kt0 * KT) / KT : 0;
   {
-    int e0[PER_T], e1[PER_T], e2[PER_T];
+    int e0[NBW], e1[NBW], e2[NBW];
     fetch_entries(0, e0);
     fetch_entries(1, e1);
     fetch_entries(2, e2);
