@@ -32,6 +32,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr size_t kDecodeLdsMax = 160 * 1024 - 256;   // dynamic LDS: a CU's 160 KB less the static part
 constexpr int kBs = 16;  // tokens per block
 constexpr uint64_t kTagLow = (1ull << 24) - 1;   // bits below a call's tag
+// The softmax reference moves only when a block's maximum exceeds it by more
+// than this many powers of two (the weights stay below 2^kLazy in between).
+constexpr float kLazy = 8.0f;
 
 __device__ __forceinline__ float wave_xor(float x, int mask) {
   return __shfl_xor(x, mask, kWave);
@@ -212,8 +215,9 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   const float sl2 = a.scale * kLog2e;
   const int P = a.max_partitions;
   float* sm_o = smem;                  // [NW][g][D]
-  float* sm_m = smem + NW * g * D;     // [NW][16]
+  float* sm_m = smem + NW * g * D;     // [NW][16] each wave's reference
   float* sm_l = sm_m + NW * 16;        // [NW][16]
+  float* sm_x = sm_l + NW * 16;        // [NW][16] each wave's maximum
 
   // One piece: blocks [bb, be) of unit (s, h); piece k of np.
   auto piece = [&](int s, int h, int L, int bb, int be, int k, int np) {
@@ -229,7 +233,12 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
       }
     }
     const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    float m_run = -INFINITY;
+    // Online softmax with a lazily moved reference: p = 2^(z - m_ref), and
+    // m_ref moves (rescaling o and l) only when a block's maximum exceeds it
+    // by more than kLazy, so p stays below 2^kLazy; m_max is the true
+    // running maximum, which the piece's statistics are reported against.
+    float m_ref = -INFINITY;
+    float m_max = -INFINITY;
     float l_run = 0.f;
     f32x4 o[KV];
 #pragma unroll
@@ -264,31 +273,48 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
           sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kd[kk], qf[kk], sc, 0, 0, 0);
         float z[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] = (grp * 4 + r < nvalid) ? sc[r] * sl2 : -INFINITY;
+        for (int r = 0; r < 4; ++r) z[r] = sc[r] * sl2;
+        const bool partial = nvalid < kBs;   // the same for the whole wave
+        if (partial) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[r] = (grp * 4 + r < nvalid) ? z[r] : -INFINITY;
+        }
         float mb = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
         mb = fmaxf(mb, wave_xor(mb, 16));
         mb = fmaxf(mb, wave_xor(mb, 32));
-        const float m_new = fmaxf(m_run, mb);
-        const float alpha = exp2f(m_run - m_new);
+        m_max = fmaxf(m_max, mb);
+        const bool grow = mb > m_ref + kLazy;
+        if (__any(grow)) {   // rare after a piece's first block
+          const float target = grow ? mb : m_ref;
+          const float alpha = exp2f(m_ref - target);   // 0 on the first block
+          l_run *= alpha;
+#pragma unroll
+          for (int m = 0; m < KV; ++m) o[m] *= alpha;
+          m_ref = target;
+        }
         float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = exp2f(z[r] - m_new);
-        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m_run = m_new;
-#pragma unroll
-        for (int m = 0; m < KV; ++m) o[m] *= alpha;
-        // Tail tokens of a partly filled block hold arbitrary bits (possibly
-        // NaN); p is 0 there but 0 * NaN is not, so clear those value words.
-        const int t0 = grp * 4;
-        const uint32_t mx = (t0 + 0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
-        const uint32_t my = (t0 + 2 < nvalid ? 0x0000ffffu : 0u) | (t0 + 3 < nvalid ? 0xffff0000u : 0u);
+        for (int r = 0; r < 4; ++r) p[r] = exp2f(z[r] - m_ref);
         const bf16x4 pf = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-#pragma unroll
-        for (int m = 0; m < KV; ++m) {
-          const u32x2 vm = u32x2{vd[m].x & mx, vd[m].y & my};
-          o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vm), pf, o[m],
-                                                           0, 0, 0);
+        {
+          // the sum of exactly the rounded weights the value product uses
+          const u32x2 pw = __builtin_bit_cast(u32x2, pf);
+          l_run += (bf16_lo(pw.x) + bf16_hi(pw.x)) + (bf16_lo(pw.y) + bf16_hi(pw.y));
         }
+        if (partial) {
+          // Tail tokens of a partly filled block hold arbitrary bits
+          // (possibly NaN); p is 0 there but 0 * NaN is not, so clear those
+          // value words.
+          const int t0 = grp * 4;
+          const uint32_t mx = (t0 + 0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
+          const uint32_t my = (t0 + 2 < nvalid ? 0x0000ffffu : 0u) | (t0 + 3 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int m = 0; m < KV; ++m) vd[m] = u32x2{vd[m].x & mx, vd[m].y & my};
+        }
+#pragma unroll
+        for (int m = 0; m < KV; ++m)
+          o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vd[m]), pf,
+                                                           o[m], 0, 0, 0);
       }
     }
 
@@ -302,17 +328,21 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
       for (int m = 0; m < KV; ++m)
         *reinterpret_cast<f32x4*>(&sm_o[(wave * g + col) * D + m * 16 + grp * 4]) = o[m];
       if (grp == 0) {
-        sm_m[wave * 16 + col] = m_run;
+        sm_m[wave * 16 + col] = m_ref;
         sm_l[wave * 16 + col] = l_run;
+        sm_x[wave * 16 + col] = m_max;
       }
     }
     __syncthreads();
     for (int idx = tid; idx < g * D; idx += NT) {
       const int c = idx / D;
       const int dd = idx - c * D;
+      // the piece's maximum; each wave's o and l are relative to its own
+      // reference, weighted by 2^(reference - M) (0 for a wave that saw no
+      // block)
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_m[v * 16 + c]);
+      for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_x[v * 16 + c]);
       float lsum = 0.f, acc = 0.f;
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
@@ -708,10 +738,10 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     // 200 for 8 waves x 4 per CU, 191 for 4 waves x 4, 194 for 1 wave x 16).
     constexpr int NW = 8, NWS = 2;
     const int nw = a.seq_prefix ? NWS : NW;
-    // wave-merge area [nw][g][D] + [nw][16] m + [nw][16] l, also used for
+    // wave-merge area [nw][g][D] + [nw][16] x 3 (reference, l, maximum), also used for
     // the piece weights of a merge ([2][g][P] + [g])
     // (the shared-prefix variant merges in a separate kernel)
-    const size_t wave_area = (size_t)nw * g * D + 2 * nw * 16;
+    const size_t wave_area = (size_t)nw * g * D + 3 * nw * 16;
     const size_t merge_area = (size_t)2 * g * a.max_partitions + g;
     const size_t words = a.seq_prefix ? wave_area : max(wave_area, merge_area);
     const size_t lds = words * sizeof(float);
