@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <atomic>
 #include <random>
 
@@ -309,6 +310,22 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
 
 namespace {
 
+// The bf16 decode kernels number the call's (sequence, KV head, block)
+// triples, and the ranges of up to 4 x decode_workgroups() workgroups over
+// them, in 32-bit arithmetic: refuse calls whose list could reach 2^31.
+int check_positions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                    int64_t P, int32_t ptok, int32_t block_size) {
+  const int64_t piece_blocks = ptok / block_size;
+  const int64_t nb = std::min<int64_t>(max_blocks_per_seq, (P - 1) * piece_blocks);
+  const int64_t list = (int64_t)num_seqs * num_kv_heads * nb;
+  const int64_t wgs = 4 * (int64_t)decode_workgroups();
+  if (list + wgs >= INT32_MAX || wgs * (piece_blocks + 1) >= INT32_MAX)
+    return fail(PKV_ERR_INVALID,
+                "%lld (sequence, KV head, block) triples in one call (2^31 at most); split the "
+                "batch", (long long)list);
+  return PKV_OK;
+}
+
 // Checks shared by the decode entries; sets *P (pieces per context the
 // partials hold) and *ptok (piece tokens) on success.
 int decode_prepare(const void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -340,7 +357,7 @@ int decode_prepare(const void* out, const void* q, const void* k_pool, const voi
     return fail(PKV_ERR_UNSUPPORTED,
                 "max_context_len %d over partition_size %d gives %lld pieces per context; use a "
                 "larger partition_size", max_context_len, *ptok, (long long)*P);
-  return PKV_OK;
+  return check_positions(num_seqs, num_kv_heads, max_blocks_per_seq, *P, *ptok, block_size);
 }
 
 pkv::DecodeArgs decode_args(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -510,6 +527,8 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   // a sequence's start block travels in 20 bits of its tagged word
   if ((int64_t)sp.count * sp.blocks >= (1 << 20))
     return fail(PKV_ERR_INVALID, "max_prefix_blocks %d too large", max_prefix_blocks);
+  rc = check_positions(num_seqs, num_kv_heads, max_blocks_per_seq, P, ptok, block_size);
+  if (rc) return rc;
   const SharedLayout lay = shared_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, P, sp.count);
   if (!workspace || workspace_bytes < lay.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,

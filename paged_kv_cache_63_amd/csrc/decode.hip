@@ -96,12 +96,12 @@ __device__ __forceinline__ float get(const float* p) {
 
 // Sum over the workgroup (all threads get the result); uses red[NW].
 template <int NW>
-__device__ __forceinline__ int64_t wg_sum(int64_t v, int64_t* red) {
+__device__ __forceinline__ int wg_sum(int v, int* red) {
   for (int k = kWave / 2; k > 0; k >>= 1) v += __shfl_xor(v, k, kWave);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
-  int64_t t = 0;
+  int t = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) t += red[i];
   return t;
@@ -109,16 +109,16 @@ __device__ __forceinline__ int64_t wg_sum(int64_t v, int64_t* red) {
 
 // Inclusive prefix sum over the workgroup's threads; *total gets the sum.
 template <int NW>
-__device__ __forceinline__ int64_t wg_scan(int64_t v, int64_t* red, int64_t* total) {
+__device__ __forceinline__ int wg_scan(int v, int* red, int* total) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int k = 1; k < kWave; k <<= 1) {
-    const int64_t u = __shfl_up(v, k, kWave);
+    const int u = __shfl_up(v, k, kWave);
     if (lane >= k) v += u;
   }
   __syncthreads();
   if (lane == kWave - 1) red[threadIdx.x / kWave] = v;
   __syncthreads();
-  int64_t before = 0, all = 0;
+  int before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     if (i < (int)(threadIdx.x / kWave)) before += red[i];
@@ -135,8 +135,8 @@ __device__ __forceinline__ int64_t wg_scan(int64_t v, int64_t* red, int64_t* tot
 template <int D, int NW, bool SHARED>
 __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int64_t red[NW];
-  __shared__ int64_t sh_first_g;
+  __shared__ int red[NW];
+  __shared__ int sh_first_g;
   __shared__ int sh_first_s;
   __shared__ int sh_lastv[2];
   constexpr int KQ = D / 32;  // QK products per block
@@ -174,29 +174,31 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
 
   // Plan, part 1: total work; empty contexts get a zero row (workgroup
   // s mod W writes it).
-  int64_t mine = 0;
+  // Positions of the (sequence, KV head, block) list fit 32 bits: the host
+  // refuses calls whose list could reach 2^31 positions.
+  int mine = 0;
   for (int s = tid; s < S; s += NT) {
     const int nb = nblocks(s);
     mine += nb;
     if (nb == 0 && s % W == w)
       for (int i = 0; i < hq * D; ++i) out[(int64_t)s * hq * D + i] = 0;
   }
-  const int64_t total = (int64_t)hkv * wg_sum<NW>(mine, red);
-  const int64_t C = max((int64_t)a.partition_blocks, (total + W - 1) / W);
-  const int64_t lo = (int64_t)w * C;
+  const int total = hkv * wg_sum<NW>(mine, red);
+  const int C = max(a.partition_blocks, (int)(((uint32_t)total + W - 1) / (uint32_t)W));
+  const int lo = w * C;   // below 2^31: w < W and (W - 1) * C < total + W
   if (lo >= total) return;
-  const int64_t hi = min(lo + C, total);
+  const int hi = min(lo + C, total);
 
   // Plan, part 2: the sequence whose units contain position lo (a prefix
   // sum over the sequences, NT at a time).
   if (tid == 0) sh_first_s = -1;
-  int64_t base = 0;
+  int base = 0;
   for (int c0 = 0; c0 < S; c0 += NT) {
     const int s = c0 + tid;
-    const int64_t v = s < S ? (int64_t)hkv * nblocks(s) : 0;
-    int64_t chunk;
-    const int64_t incl = wg_scan<NW>(v, red, &chunk);
-    const int64_t st = base + incl - v;
+    const int v = s < S ? hkv * nblocks(s) : 0;
+    int chunk;
+    const int incl = wg_scan<NW>(v, red, &chunk);
+    const int st = base + incl - v;
     if (v > 0 && st <= lo && lo < st + v) {
       sh_first_s = s;
       sh_first_g = st;
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
     base += chunk;
   }
   int s = sh_first_s;
-  int64_t G = sh_first_g;
+  int G = sh_first_g;
 
   const uint16_t* qp = (const uint16_t*)a.q;
   const uint16_t* kpool = (const uint16_t*)a.k_pool;
@@ -429,11 +431,17 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
     const int st = start_block(s, nb_all);
     const int nb = nb_all - st;
     for (int h = 0; h < hkv; ++h) {
-      const int64_t Gh = G + (int64_t)h * nb;
-      const int64_t a0 = max(lo, Gh), a1 = min(hi, Gh + nb);
+      const int Gh = G + h * nb;
+      const int a0 = max(lo, Gh), a1 = min(hi, Gh + nb);
       if (a0 < a1) {
-        const int k = (int)(w - Gh / C);
-        const int np = (int)((Gh + nb - 1) / C - Gh / C + 1);
+        // A unit inside the range is one piece; only the range's first and
+        // last unit can be split, and only they need the divisions.
+        int k = 0, np = 1;
+        if (Gh < lo || Gh + nb > hi) {
+          const int first = (int)((uint32_t)Gh / (uint32_t)C);
+          k = w - first;
+          np = (int)((uint32_t)(Gh + nb - 1) / (uint32_t)C) - first + 1;
+        }
         piece(s, h, L, st + (int)(a0 - Gh), st + (int)(a1 - Gh), k, np);
         if (!SHARED && np > 1 && n_pend < 2) {
           pend_s[n_pend] = s;
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
         }
       }
     }
-    G += (int64_t)hkv * nb;
+    G += hkv * nb;
     ++s;
   }
   if (n_pend == 0) return;
