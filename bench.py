@@ -475,9 +475,10 @@ def run_shared(args, case, torch, lib, alloc_cls):
     rows_s = np.arange(S)
     groups = None
     if not args.plain_decode:
+        from paged_kv_cache_63_amd import shared_prefix_groups
         # the shared prompt's blocks lead every table for the whole run: the
         # groups are found once, from the tables the allocator holds
-        groups = lib.shared_prefix_groups(alloc.tables[rows], alloc.lens[rows] + 1)
+        groups = lib.groups_to_device(shared_prefix_groups(alloc.tables[rows], alloc.lens[rows] + 1))
         ws = torch.zeros(lib.paged_attention_decode_shared_workspace_size(
             S, hq, hkv, d, maxb * 16, 0, len(groups[2]), groups[3], groups[4]),
             dtype=torch.uint8, device=dev)

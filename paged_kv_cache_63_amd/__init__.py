@@ -13,7 +13,8 @@
   is missing; there is no other implementation to fall back to.
 """
 
-from .allocator import BlockAllocator, OutOfBlocks, kv_bytes_per_token  # noqa: F401
+from .allocator import (BlockAllocator, OutOfBlocks, kv_bytes_per_token,  # noqa: F401
+                        shared_prefix_groups)
 from .prefix_cache import PrefixCachingAllocator, block_hash  # noqa: F401
 from .radix_cache import RadixCache  # noqa: F401
 

@@ -11,6 +11,7 @@ Function names and argument meanings follow ``include/pagedkv.h``.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -309,7 +310,8 @@ def paged_attention_decode_shared(out, q, k_pool, v_pool, block_tables, context_
                                   workspace=None):
     """``groups``: ``(group_offsets, group_seqs, group_prefix_blocks, max_group_size,
     max_prefix_blocks)`` -- three int32 device tensors and two host ints, as
-    :func:`shared_prefix_groups` returns them."""
+    :func:`groups_to_device` makes them from the host grouping
+    (``allocator.shared_prefix_groups``)."""
     nb, hkv, bs, d, dt = _pools(k_pool, v_pool)
     offs, seqs, pblk, max_size, max_pb = groups
     _dev(out, q, k_pool, v_pool, block_tables, context_lens, offs, seqs, pblk)
@@ -338,43 +340,14 @@ def paged_attention_decode_shared(out, q, k_pool, v_pool, block_tables, context_
     return workspace
 
 
-def shared_prefix_groups(tables, lens, block_size=16, min_blocks=1, device=None):
-    """Groups for :func:`paged_attention_decode_shared` from host block tables
-    (numpy int32 ``[S][max_blocks]``) and context lengths: sequences whose
-    first table entry is the same physical block form a group, whose prefix
-    is the longest run of leading entries they all share, cut so that every
-    member keeps its last block for itself.  Groups of one member, or whose
-    prefix is shorter than ``min_blocks``, are left out.  Host-side work on
-    the tables the allocator already holds; returns the ``groups`` tuple with
-    the arrays on ``device``."""
-    import numpy as np
-    tables = np.asarray(tables)
-    lens = np.asarray(lens).astype(np.int64)
-    nb = (lens + block_size - 1) // block_size
-    usable = np.where(lens > 0, (lens - 1) // block_size, 0)   # blocks before the last one
-    first = np.where(nb > 0, tables[:, 0], -1)
-    order = np.argsort(first, kind="stable")
-    offs, seqs, pblk = [0], [], []
-    i = 0
-    while i < len(order):
-        j = i
-        while j < len(order) and first[order[j]] == first[order[i]]:
-            j += 1
-        members = order[i:j]
-        if first[order[i]] >= 0 and len(members) > 1:
-            limit = int(usable[members].min())
-            rows = tables[members, :limit]
-            same = (rows == rows[0]).all(axis=0)
-            k = limit if same.all() else int(np.argmin(same))
-            if k >= min_blocks:
-                seqs += members.tolist()
-                pblk.append(k)
-                offs.append(len(seqs))
-        i = j
+def groups_to_device(groups, device=None):
+    """The ``groups`` tuple of :func:`allocator.shared_prefix_groups` (three
+    int32 numpy arrays and two ints) with its arrays as int32 tensors on the
+    GPU, as :func:`paged_attention_decode_shared` takes it."""
+    offs, seqs, pblk, max_size, max_pb = groups
     dev = device if device is not None else "cuda"
-    t = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)
-    return (t(offs), t(seqs), t(pblk), max((offs[g + 1] - offs[g] for g in range(len(pblk))),
-                                           default=0), max(pblk, default=0))
+    t = lambda x: torch.as_tensor(np.asarray(x, dtype=np.int32)).to(dev)
+    return (t(offs), t(seqs), t(pblk), int(max_size), int(max_pb))
 
 
 def paged_attention_extend(out, q, cu_seqlens_q, seq_lens, k_pool, v_pool, block_tables,

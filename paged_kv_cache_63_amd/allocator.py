@@ -498,3 +498,47 @@ class BlockAllocator:
     def _holders(self) -> np.ndarray:
         """References held outside sequence tables, per block (a cache's)."""
         return np.zeros(self.num_blocks, dtype=np.int64)
+
+
+def shared_prefix_groups(tables, lens, block_size: int = 16, min_blocks: int = 1):
+    """Groups of sequences that share the leading physical blocks of their
+    tables, for the shared-prefix decode: sharing a prefix is a pointer
+    change, every sharer's table naming the same physical blocks ("Paged
+    Attention for Efficient Memory Management", The Daily Triptych, "Look
+    closer / Sharing is a pointer change").
+
+    ``tables``: ``[S][max_blocks]`` block tables; ``lens``: ``[S]`` context
+    lengths.  Sequences whose first table entry is the same physical block
+    form a group; its prefix is the longest run of leading entries all of
+    them hold, cut so that every member keeps the block with its last token
+    to itself.  Groups of one member, or with a prefix shorter than
+    ``min_blocks``, are left out.  Returns ``(group_offsets, group_seqs,
+    group_prefix_blocks, max_group_size, max_prefix_blocks)``: three int32
+    arrays (members of group i are ``group_seqs[group_offsets[i] :
+    group_offsets[i + 1]]``) and two ints."""
+    tables = np.asarray(tables)
+    lens = np.asarray(lens).astype(np.int64)
+    nb = (lens + block_size - 1) // block_size
+    usable = np.where(lens > 0, (lens - 1) // block_size, 0)   # blocks before the last one
+    first = np.where(nb > 0, tables[:, 0], -1)
+    order = np.argsort(first, kind="stable")
+    offs, seqs, pblk = [0], [], []
+    i = 0
+    while i < len(order):
+        j = i
+        while j < len(order) and first[order[j]] == first[order[i]]:
+            j += 1
+        members = order[i:j]
+        if first[order[i]] >= 0 and len(members) > 1:
+            limit = int(usable[members].min())
+            rows = tables[members, :limit]
+            same = (rows == rows[0]).all(axis=0)
+            k = limit if same.all() else int(np.argmin(same))
+            if k >= min_blocks:
+                seqs += members.tolist()
+                pblk.append(k)
+                offs.append(len(seqs))
+        i = j
+    sizes = [offs[g + 1] - offs[g] for g in range(len(pblk))]
+    return (np.asarray(offs, np.int32), np.asarray(seqs, np.int32), np.asarray(pblk, np.int32),
+            max(sizes, default=0), max(pblk, default=0))

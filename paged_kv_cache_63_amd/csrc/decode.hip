@@ -458,11 +458,30 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
 
   // Publish this workgroup's split pieces (once, at the end, so that the
   // stores have long completed); the piece of a unit that arrives last
-  // merges the unit.  Pieces are written and read with agent-coherent
-  // accesses (they write through, and read past, the per-XCD L2 caches,
-  // which are not coherent with one another), every thread's stores are
-  // complete before the workgroup counts itself in, and the arrival count is
-  // an atomic add: no cache-wide fence is needed.
+  // merges the unit.
+  //
+  // Memory ordering.  The pieces' o, m and l travel between workgroups that
+  // may sit on different XCDs, whose L2 caches are not coherent with one
+  // another.  They are not ordered by a release/acquire pair (in HIP's
+  // model that is a fence: on gfx950 an agent-scope release writes back
+  // and an acquire invalidates this XCD's whole L2, which made the kernel
+  // about 4x slower).  Instead every access to them is an agent-scope
+  // atomic (put/get: relaxed, compiled to sc1 stores that write through
+  // the L2 and sc1 loads that read past it), and the order comes from the
+  // hardware:
+  //   1. `s_waitcnt vmcnt(0)` below returns only when each of this thread's
+  //      write-through stores has been acknowledged by the memory side,
+  //      where every XCD's agent-scope accesses meet;
+  //   2. the barrier then holds every thread until all have passed step 1,
+  //      so all of the workgroup's piece data is at the memory side before
+  //      thread tid < n_pend counts the piece in;
+  //   3. the count is an agent-scope compare-and-swap, performed at that
+  //      same memory side, so the workgroup that reads the final count has
+  //      seen every earlier count and hence every earlier piece's stores;
+  //   4. that workgroup's merge reads the pieces with sc1 loads, which do
+  //      not return stale lines from its own L2.
+  // This leans on gfx950's cache behaviour rather than on the language's
+  // memory model, and holds only with the accesses kept as they are.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid < n_pend) {

@@ -8,7 +8,7 @@ import torch
 
 from gpu_helpers import f64_of, i32, poisoned_pools, to_dev
 from oracle import attention, block_manager, paging
-from paged_kv_cache_63_amd import BlockAllocator, _lib
+from paged_kv_cache_63_amd import BlockAllocator, _lib, shared_prefix_groups
 from workloads import normal_words
 
 pytestmark = pytest.mark.gpu
@@ -126,7 +126,7 @@ def _shared(lib, scale, groups, partition_size=0, workspace=None):
 
 def test_helper_groups(case):
     lib, ref, scale, want = case
-    groups = _lib.shared_prefix_groups(lib["tables"], lib["lens"])
+    groups = _lib.groups_to_device(shared_prefix_groups(lib["tables"], lib["lens"]))
     offs = groups[0].cpu().tolist()
     assert len(offs) == 3 and groups[4] == 8       # groups of PA's and PB's families
     got, _ = _shared(lib, scale, groups)
