@@ -25,7 +25,9 @@
  *    Every floating-point tensor of one call has that dtype, except the
  *    decode workspace (fp32).
  *  - block_size: 16 (the pages' default, "PagedAttention 与 RadixAttention",
- *    section "PagedAttention").  head_dim: 64 or 128.  num_q_heads must be
+ *    section "PagedAttention") or 32 (the alternative they name, "PagedAttention
+ *    and RadixAttention: Let's Talk About KV Cache", section "PagedAttention:
+ *    Memory Like an Operating System").  head_dim: 64 or 128.  num_q_heads must be
  *    a multiple of num_kv_heads with a group of at most 16 query heads per
  *    KV head (query head j uses KV head j / (num_q_heads / num_kv_heads)).
  *  - Device memory is addressed with 64-bit offsets: pools of any size.
@@ -37,9 +39,10 @@
  *            -- values are stored transposed inside a block: one row of
  *               block_size tokens per channel, in which the token at
  *               offset `off` sits at position v_pos(off) = off with bits
- *               2 and 3 exchanged (order 0-3, 8-11, 4-7, 12-15; the map is
- *               its own inverse).  This is the order in which the matrix
- *               cores consume a block's tokens, two 8-byte halves per lane.
+ *               2 and 3 exchanged (order 0-3, 8-11, 4-7, 12-15, then the
+ *               same for 16-31 in a 32-token block; the map is its own
+ *               inverse).  This is the order in which the matrix cores
+ *               consume a block's tokens, two 8-byte halves per lane.
  *  A slot is phys_block * block_size + offset_in_block.
  *
  * Safety: kernels never touch memory outside the ranges the arguments
@@ -313,8 +316,8 @@ size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t nu
  * min(prefix_blocks, (context_len - 1) / block_size) table entries must be
  * the first member's (the call reads the prefix blocks from the first
  * member's row only), and the first member must hold all prefix_blocks.
- * Otherwise the result is undefined, but every access stays inside the pool.  fp32 inputs, or no
- * groups, run paged_attention_decode unchanged.  Errors as
+ * Otherwise the result is undefined, but every access stays inside the pool.  fp32 inputs,
+ * block_size 32, or no groups, run paged_attention_decode unchanged.  Errors as
  * paged_attention_decode; PKV_ERR_UNSUPPORTED when the merge weights,
  * 2 x group x (P + NS) + group fp32 words, exceed the LDS; PKV_ERR_INVALID
  * when the prefix splits cover 2^20 blocks or more (the start block would

@@ -32,7 +32,8 @@ int elem_bytes(int32_t dtype) { return dtype == PKV_DTYPE_FP32 ? 4 : dtype == PK
 // Shared shape checks; returns PKV_OK or an error code (message set).
 int check_common(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype) {
   if (!elem_bytes(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported (0=fp32, 1=bf16)", dtype);
-  if (block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "block_size %d not supported (16)", block_size);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not supported (16 or 32)", block_size);
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
   if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "num_kv_heads must be positive");
@@ -267,8 +268,8 @@ int upload_and_append_tables(void* dst, const void* staging, int64_t bytes, int6
     u.n = num_updates;
   }
   rc = pkv::launch_upload_append(d, sv, bytes, slots_offset, k_new, v_new, num_tokens, k_pool,
-                                 v_pool, num_blocks, num_kv_heads, head_dim, elem_bytes(dtype),
-                                 (hipStream_t)stream, u);
+                                 v_pool, num_blocks, num_kv_heads, head_dim, block_size,
+                                 elem_bytes(dtype), (hipStream_t)stream, u);
   return rc ? fail(rc, "upload_and_append launch failed") : ok();
 }
 
@@ -315,8 +316,10 @@ namespace {
 // them, in 32-bit arithmetic: refuse calls whose list could reach 2^31.
 int check_positions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq,
                     int64_t P, int32_t ptok, int32_t block_size) {
-  const int64_t piece_blocks = ptok / block_size;
-  const int64_t nb = std::min<int64_t>(max_blocks_per_seq, (P - 1) * piece_blocks);
+  // the kernels count 16-token granules (a 32-token block is two)
+  const int64_t piece_blocks = ptok / 16;
+  const int64_t nb = std::min<int64_t>((int64_t)max_blocks_per_seq * (block_size / 16),
+                                       (P - 1) * piece_blocks);
   const int64_t list = (int64_t)num_seqs * num_kv_heads * nb;
   const int64_t wgs = 4 * (int64_t)decode_workgroups();
   if (list + wgs >= INT32_MAX || wgs * (piece_blocks + 1) >= INT32_MAX)
@@ -385,7 +388,8 @@ pkv::DecodeArgs decode_args(void* out, const void* q, const void* k_pool, const 
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
-  a.partition_blocks = ptok / block_size;
+  a.partition_blocks = ptok / 16;   // in 16-token granules
+  a.bs_shift = block_size == 32 ? 1 : 0;
   a.max_partitions = (int32_t)P;
   a.num_workgroups = decode_workgroups();
   a.scale = scale;
@@ -495,8 +499,10 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   if (rc) return rc;
   if (num_groups < 0 || max_group_size < 0 || max_prefix_blocks < 0)
     return fail(PKV_ERR_INVALID, "negative group argument");
-  if (dtype != PKV_DTYPE_BF16 || num_groups == 0 || max_group_size == 0 || max_prefix_blocks == 0)
-    // nothing shared (or fp32, whose path has no prefix pass): the plain decode
+  if (dtype != PKV_DTYPE_BF16 || num_groups == 0 || max_group_size == 0 ||
+      max_prefix_blocks == 0 || block_size != 16)
+    // nothing shared (or fp32, or 32-token blocks, which have no prefix
+    // pass): the plain decode
     return paged_attention_decode(out, q, k_pool, v_pool, num_blocks, block_tables,
                                   max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                                   num_q_heads, num_kv_heads, head_dim, block_size, scale,
@@ -639,6 +645,7 @@ int paged_attention_extend(void* out, const void* q, const int32_t* cu_seqlens_q
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
+  a.block_size = block_size;
   a.scale = scale;
   rc = pkv::launch_extend(a, dtype, (hipStream_t)stream);
   return rc ? fail(rc, "extend launch failed: %s", hipGetErrorString(hipGetLastError())) : ok();

@@ -62,7 +62,7 @@ int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st,
                   TableUpdates u = TableUpdates{});
 int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slots_offset,
                          const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
-                         void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d,
+                         void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d, int32_t bs,
                          int32_t elem_bytes, hipStream_t st, TableUpdates u = TableUpdates{});
 int launch_swap_blocks(void* dst_k, void* dst_v, int32_t num_dst, const void* src_k,
                        const void* src_v, int32_t num_src, const int32_t* mapping,
@@ -94,7 +94,8 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t partition_blocks;  // smallest piece (bf16) / partition (fp32), in blocks
+  int32_t partition_blocks;  // smallest piece (bf16) / partition (fp32), in 16-token granules
+  int32_t bs_shift;          // log2(block_size / 16): a table entry covers 16 << bs_shift tokens
   int32_t max_partitions;    // P: pieces per (sequence, query head) the workspace holds
   int32_t num_workgroups;    // bf16 grid
   float scale;
@@ -141,6 +142,7 @@ struct ExtendArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
+  int32_t block_size;   // 16 or 32
   float scale;
 };
 

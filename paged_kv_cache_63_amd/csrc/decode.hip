@@ -50,7 +50,7 @@ __device__ __forceinline__ int clamp_block(int b, int num_blocks) {
 __device__ __forceinline__ int usable_len(const DecodeArgs& a, int s) {
   int L = a.context_lens[s];
   L = L < 0 ? 0 : L;
-  const int cap_tab = a.max_blocks_per_seq * kBs;
+  const int cap_tab = a.max_blocks_per_seq * (kBs << a.bs_shift);
   // the workspace holds max_partitions pieces per unit: at most
   // ceil(nb / partition_blocks) + 1 of them for nb blocks
   const int cap_part = (a.max_partitions - 1) * a.partition_blocks * kBs;
@@ -132,7 +132,7 @@ __device__ __forceinline__ int wg_scan(int v, int* red, int* total) {
 // stay resident, the number the grid is sized for.
 // SHARED: the shared-prefix variant (seq_prefix and the prefix partials are
 // read); a template flag so that the plain decode's code is unaffected.
-template <int D, int NW, bool SHARED>
+template <int D, int NW, bool SHARED, int BS>
 __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int red[NW];
@@ -213,7 +213,16 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   const uint16_t* qp = (const uint16_t*)a.q;
   const uint16_t* kpool = (const uint16_t*)a.k_pool;
   const uint16_t* vpool = (const uint16_t*)a.v_pool;
-  const int64_t head_elems = (int64_t)kBs * D;  // one (block, head) slab
+  // The kernel walks 16-token granules; a table entry covers 1 << sh of
+  // them (block_size 16 << sh).  Granule b is part b & (2^sh - 1) of the
+  // entry b >> sh: its keys are that part's 16 rows of the (block, head) K
+  // slab, its values the same 16 positions of each channel row of the V
+  // slab (channel rows of 16 << sh tokens).
+  constexpr int sh = BS == 32 ? 1 : 0;
+  static_assert(BS == 16 || BS == 32, "block sizes 16 and 32");
+  const int64_t head_elems = (int64_t)kBs * D;           // one granule of one head
+  const int64_t slab_elems = head_elems << sh;           // one (block, head) slab
+  const int vrow = kBs << sh;                            // V channel row, elements
   const float sl2 = a.scale * kLog2e;
   const int P = a.max_partitions;
   float* sm_o = smem;                  // [NW][g][D]
@@ -251,14 +260,16 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
     for (int i0 = 0; i0 < cnt; i0 += kWave) {
       const int n_here = min(kWave, cnt - i0);
       int my_entry = 0;
-      if (lane < n_here) my_entry = clamp_block(trow[bb + wave + (i0 + lane) * NW], a.num_blocks);
+      if (lane < n_here)
+        my_entry = clamp_block(trow[(bb + wave + (i0 + lane) * NW) >> sh], a.num_blocks);
       for (int i = 0; i < n_here; ++i) {
         const int b = bb + wave + (i0 + i) * NW;
         const int phys = __builtin_amdgcn_readlane(my_entry, i);
-        const int64_t hb = ((int64_t)phys * hkv + h) * head_elems;
-        const uint16_t* kr = kpool + hb + col * D + grp * 8;    // token row = col
+        const int part = b & ((1 << sh) - 1);
+        const int64_t hb = ((int64_t)phys * hkv + h) * slab_elems;
+        const uint16_t* kr = kpool + hb + part * head_elems + col * D + grp * 8;   // token row = col
         // channel row = col; tokens 4grp..4grp+3 sit at v_pos(4grp)
-        const uint16_t* vr = vpool + hb + col * kBs + v_pos(grp * 4);
+        const uint16_t* vr = vpool + hb + col * vrow + part * kBs + v_pos(grp * 4);
         bf16x8 kd[KQ];
         u32x2 vd[KV];
 #pragma unroll
@@ -267,7 +278,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
               bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + kk * 32)));
 #pragma unroll
         for (int m = 0; m < KV; ++m)
-          vd[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vr + m * 16 * kBs));
+          vd[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vr + m * 16 * vrow));
         const int nvalid = L - b * kBs;   // tokens of this block inside the context
         f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -549,11 +560,16 @@ __global__ __launch_bounds__(kWave) void decode_f32_kernel(DecodeArgs a) {
     for (int i = 0; i < DPL; ++i) o[j][i] = 0.f;
   }
 
+  // 16-token granules; a table entry covers 1 << sh of them (as in the bf16
+  // kernel)
+  const int sh = a.bs_shift;
+  const int vrow = kBs << sh;
   for (int b = b0; b < b1; ++b) {
-    const int phys = clamp_block(trow[b], a.num_blocks);
-    const int64_t base = ((int64_t)phys * hkv + h) * kBs * D;
-    const float* kb = kpool + base;
-    const float* vb = vpool + base;
+    const int phys = clamp_block(trow[b >> sh], a.num_blocks);
+    const int part = b & ((1 << sh) - 1);
+    const int64_t base = ((int64_t)phys * hkv + h) * (kBs << sh) * D;
+    const float* kb = kpool + base + part * kBs * D;
+    const float* vb = vpool + base + part * kBs;
     const int nvalid = min(kBs, L - b * kBs);
     for (int idx = lane; idx < kBs * g; idx += kWave) {
       const int t = idx & (kBs - 1);
@@ -578,7 +594,7 @@ __global__ __launch_bounds__(kWave) void decode_f32_kernel(DecodeArgs a) {
         const float pt = expf(sc_s[j][t] - m_new);
         psum += pt;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pt, vb[(lane + i * kWave) * kBs + v_pos(t)], acc[i]);
+        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pt, vb[(lane + i * kWave) * vrow + v_pos(t)], acc[i]);
       }
       l_run[j] = l_run[j] * alpha + psum;
       m_run[j] = m_new;
@@ -773,9 +789,13 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     const size_t words = a.seq_prefix ? wave_area : max(wave_area, merge_area);
     const size_t lds = words * sizeof(float);
     if (lds > kDecodeLdsMax) return -2;
-    auto kern = a.seq_prefix ? decode_bf16_kernel<D, NWS, true> : decode_bf16_kernel<D, NW, false>;
-    static std::atomic<uint64_t> attr_set[2];   // per variant, one bit per device
-    if (raise_lds_limit((const void*)kern, &attr_set[a.seq_prefix != nullptr])) return -4;
+    // (the shared-prefix entry runs only with 16-token blocks)
+    auto kern = a.seq_prefix ? decode_bf16_kernel<D, NWS, true, 16>
+                : a.bs_shift ? decode_bf16_kernel<D, NW, false, 32>
+                             : decode_bf16_kernel<D, NW, false, 16>;
+    const int variant = a.seq_prefix ? 1 : a.bs_shift ? 2 : 0;
+    static std::atomic<uint64_t> attr_set[3];   // per variant, one bit per device
+    if (raise_lds_limit((const void*)kern, &attr_set[variant])) return -4;
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     // (tagged words, nothing to clear)
     kern<<<a.seq_prefix ? 4 * a.num_workgroups : a.num_workgroups, nw * kWave, lds, st>>>(a);

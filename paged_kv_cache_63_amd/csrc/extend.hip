@@ -139,26 +139,40 @@ __device__ __forceinline__ void lds_dma16_kv(const uint8_t* kbase, uint32_t koff
 // may see no key of a split at all, so the exponent reference of such a row
 // is taken as 0 instead of -inf.  Output: the normalised partial (o, m in
 // natural-log units, l) per (member, query head, split).
-template <int D, bool PREFIX, typename Args>
+template <int D, bool PREFIX, typename Args, int BS>
 __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tiles_per_unit,
                                                                 int units) {
   constexpr int NW = 8;
   constexpr int HALF = NW / 2;            // waves per group: one per SIMD
   constexpr int RPW = 32;                 // query rows per wave
   constexpr int ROWS = NW * RPW;
-  constexpr int NBT = 4;                  // blocks per key tile
-  constexpr int KT = NBT * kBs;           // keys per tile
+  // A key tile is 64 keys: four 16-key sub-blocks (the unit of the
+  // products), i.e. NBT table blocks of BS tokens (BS = 16 or 32).
+  constexpr int NSB = 4;                  // 16-key sub-blocks per key tile
+  constexpr int SPB = BS / kBs;           // sub-blocks per table block
+  constexpr int NBT = NSB / SPB;          // table blocks per key tile
+  constexpr int KT = NSB * kBs;           // keys per tile
   constexpr int KS = D / 16;              // QK k-steps per 32-key chunk
   constexpr int DT = D / 32;              // 32-channel tiles of O
   constexpr int ROWB = D * 2;             // bytes of one key row
   constexpr int CPR = D / 8;              // 16-byte chunks per key row
   constexpr int SWZ = 16 / CPR;           // consecutive key rows sharing one swizzle value
-  constexpr int BLKB = kBs * ROWB;        // bytes of one (block, head) slab
-  constexpr int TILEB = NBT * BLKB;       // bytes of a K (or V) tile
+  constexpr int SUBB = kBs * ROWB;        // bytes of one 16-key sub-block of one head
+  constexpr int BLKB = BS * ROWB;         // bytes of one (block, head) slab
+  constexpr int VROWB = BS * 2;           // bytes of one V channel row of a slab
+  constexpr int TILEB = NSB * SUBB;       // bytes of a K (or V) tile
   constexpr int SEGS = TILEB / 16 / kWave;  // 64-chunk segments per K (or V) tile
   constexpr int PER_T = 2 * SEGS / NW;    // direct-to-LDS loads per thread per tile
   constexpr int NST = 5;                  // LDS ring stages (160 KB for D = 128)
   static_assert(PER_T * NW == 2 * SEGS, "tile must split evenly over the waves");
+  static_assert(BS == 16 || BS == 32, "block sizes 16 and 32");
+  // V rows in LDS: the 16-byte chunks of channel row c are permuted by an
+  // XOR with vswz(c), so that the 16 lanes of one read phase (channels
+  // c..c+15, the same chunk) hit 16 distinct 4-bank groups: 32-byte rows
+  // (BS 16) repeat the banks every 8 channels, 64-byte rows (BS 32) every 4.
+  auto vswz = [](int c) -> int {
+    return BS == 16 ? (((c >> 2) ^ (c >> 3)) & 1) : ((c >> 2) & 3);
+  };
   // Rescale the accumulators only when a row's maximum has grown by more
   // than this many powers of two since the reference used for its
   // exponentials (the exponentials stay below 2^kLazy in between).
@@ -185,7 +199,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     n = a.cu_seqlens_q[r + 1] - q0;
     L = a.seq_lens[r];
     if (n <= 0 || row0 >= n * g || q0 < 0 || q0 + n > a.total_q) return;
-    if (L > a.max_blocks_per_seq * kBs) L = a.max_blocks_per_seq * kBs;
+    if (L > a.max_blocks_per_seq * BS) L = a.max_blocks_per_seq * BS;
     P = L - n;
     if (P < 0) return;
   } else {
@@ -225,7 +239,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
   const bool lead = wave < HALF;
   const int c32 = lane & 31;    // A/B row-or-column, C column
   const int G = lane >> 5;      // k-slot group / C row group
-  const int nblk = (L + kBs - 1) / kBs;
+  const int nblk = (L + BS - 1) / BS;   // table blocks holding keys 0 .. L-1
   const_i32* trow = (const_i32*)(a.block_tables + (int64_t)r * a.max_blocks_per_seq);
 
   // Rows of this workgroup and their last visible key.
@@ -303,9 +317,11 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     const int within = c0 - blk * (BLKB / 16) + lane;
     const int row = within / CPR;
     const int pos = within - row * CPR;
-    src_off_k[i] = (uint32_t)(h * BLKB + (row * CPR + (pos ^ ((row / SWZ) % CPR))) * 16);
-    const int vrow = within >> 1;
-    src_off_v[i] = (uint32_t)(h * BLKB + (within ^ (((vrow >> 2) ^ (vrow >> 3)) & 1)) * 16);
+    src_off_k[i] = (uint32_t)(h * BLKB + (row * CPR + (pos ^ (((row & 15) / SWZ) % CPR))) * 16);
+    // V: LDS chunk q' of channel row c holds the slab's chunk q' ^ vswz(c)
+    constexpr int CPV = VROWB / 16;       // 16-byte chunks per V channel row
+    const int vc = within / CPV;
+    src_off_v[i] = (uint32_t)(h * BLKB + (vc * CPV + ((within % CPV) ^ vswz(vc))) * 16);
     src_blk[i] = blk;
   }
   const uint32_t blk_stride = (uint32_t)(hkv * BLKB);   // bytes between physical blocks
@@ -333,9 +349,13 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     const int f = (row / SWZ) % CPR;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      koff[ks] = (uint32_t)((c32 >> 4) * BLKB + row * ROWB + (((ks * 2 + G) ^ f) * 16));
+      koff[ks] = (uint32_t)((c32 >> 4) * SUBB + row * ROWB + (((ks * 2 + G) ^ f) * 16));
   }
-  const uint32_t voff = (uint32_t)(TILEB + c32 * 32 + ((G ^ (((c32 >> 2) ^ (c32 >> 3)) & 1)) * 16));
+  // V: sub-block part p of a slab is chunks 2p, 2p+1 of each channel row
+  uint32_t voff[SPB];
+#pragma unroll
+  for (int p = 0; p < SPB; ++p)
+    voff[p] = (uint32_t)(TILEB + c32 * VROWB + (((2 * p + G) ^ vswz(c32)) * 16));
 
   const float c2 = a.scale * kLog2e;   // scores -> base-2 exponent units
   float m_ref = -INFINITY;
@@ -350,22 +370,24 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
   f32x16 sc[2];
-  bf16x8 pf[NBT];
+  bf16x8 pf[NSB];
 
   // Matrix-phase streams.  Fragment reads and MFMAs are interleaved with
   // a fixed lookahead, so LDS latency hides behind the matrix core and only
   // a few fragments are live at once.
   // PV reads: V fragment (block b, channel tile dt) for i = b*DT + dt.
   // QK reads: K fragment (k-step ks, 32-key chunk ch) for i = ks*2 + ch.
-  constexpr int NPV = NBT * DT;
+  constexpr int NPV = NSB * DT;
   constexpr int NQK = 2 * KS;
   constexpr int LA = 6;          // lookahead of the QK-only stream
   constexpr int NPRE = NPV / 2;  // V fragments read at the end of the vector phase
   auto vread = [&](int st, int i) {
-    return *reinterpret_cast<const bf16x8*>(kv_s[st] + voff + (i / DT) * BLKB + (i % DT) * 32 * 32);
+    const int b = i / DT;   // sub-block
+    return *reinterpret_cast<const bf16x8*>(kv_s[st] + voff[b % SPB] + (b / SPB) * BLKB +
+                                            (i % DT) * 32 * VROWB);
   };
   auto kread = [&](int st, int i) {
-    return *reinterpret_cast<const bf16x8*>(kv_s[st] + koff[i / 2] + (i % 2) * 2 * BLKB);
+    return *reinterpret_cast<const bf16x8*>(kv_s[st] + koff[i / 2] + (i % 2) * 2 * SUBB);
   };
   auto pv_mfma = [&](int i, bf16x8 f) {
     o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / DT], o[i % DT], 0, 0, 0);
@@ -413,7 +435,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) pv_mfma(i, vpre[i]);
 #pragma unroll
-    for (int b = 0; b < NBT; ++b) sum_mfma(b);
+    for (int b = 0; b < NSB; ++b) sum_mfma(b);
 #pragma unroll
     for (int i = NPRE; i < NPV; ++i) pv_mfma(i, fr[i - NPRE]);
 #pragma unroll
@@ -423,7 +445,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NPRE + NBT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NPRE + NSB, 0);
     __builtin_amdgcn_s_setprio(0);
   };
   // QK alone (first tile): LA reads, then (MFMA, read) pairs.
@@ -479,7 +501,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     float nm = -m_ref;
     if constexpr (PREFIX) nm = m_ref == -INFINITY ? 0.f : nm;   // a row with no key yet
 #pragma unroll
-    for (int b = 0; b < NBT; ++b) {
+    for (int b = 0; b < NSB; ++b) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[b >> 1][(b & 1) * 8 + e], c2, nm));
@@ -489,7 +511,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     // The probabilities are computed in this (vector) phase, not in the
     // matrix phase that consumes them.
 #pragma unroll
-    for (int b = 0; b < NBT; ++b) materialize(pf[b]);
+    for (int b = 0; b < NSB; ++b) materialize(pf[b]);
   };
 
   // PV alone (the last tile of the workgroup).  V^T operand of block b,
@@ -504,7 +526,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     for (int i = 0; i < NPV; ++i) fr[i] = vread(sp, i);
     if (kbase + KT > L) {
 #pragma unroll
-      for (int b = 0; b < NBT; ++b) {
+      for (int b = 0; b < NSB; ++b) {
         uint32_t mk[4];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -523,7 +545,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
 #pragma unroll
     for (int i = 0; i < NPV; ++i) pv_mfma(i, fr[i]);
 #pragma unroll
-    for (int b = 0; b < NBT; ++b) sum_mfma(b);
+    for (int b = 0; b < NSB; ++b) sum_mfma(b);
   };
 
   // Slots: waves 0..3 run matrix phase j in slot 2j and vector phase j in
@@ -676,7 +698,8 @@ __global__ __launch_bounds__(kWave) void extend_f32_kernel(ExtendArgs a) {
   const int n = a.cu_seqlens_q[r + 1] - q0;
   if (i >= n || q0 < 0 || q0 + n > a.total_q) return;
   int L = a.seq_lens[r];
-  if (L > a.max_blocks_per_seq * kBs) L = a.max_blocks_per_seq * kBs;
+  const int bsz = a.block_size;
+  if (L > a.max_blocks_per_seq * bsz) L = a.max_blocks_per_seq * bsz;
   const int P = L - n;
   if (P < 0) return;
   const int ctx = P + i + 1;
@@ -696,13 +719,16 @@ __global__ __launch_bounds__(kWave) void extend_f32_kernel(ExtendArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[j][e] = 0.f;
   }
+  // 16-token granules; granule b is part b % (bsz/16) of table block b / (bsz/16)
+  const int spb = bsz / kBs;
   const int nb = (ctx + kBs - 1) / kBs;
   for (int b = 0; b < nb; ++b) {
-    int phys = trow[b];
+    int phys = trow[b / spb];
     phys = (phys >= 0 && phys < a.num_blocks) ? phys : 0;
-    const int64_t base = ((int64_t)phys * hkv + h) * kBs * D;
-    const float* kb = kpool + base;
-    const float* vb = vpool + base;
+    const int part = b % spb;
+    const int64_t base = ((int64_t)phys * hkv + h) * bsz * D;
+    const float* kb = kpool + base + part * kBs * D;
+    const float* vb = vpool + base + part * kBs;
     const int nvalid = min(kBs, ctx - b * kBs);
     for (int idx = lane; idx < kBs * g; idx += kWave) {
       const int t = idx & (kBs - 1);
@@ -726,7 +752,7 @@ __global__ __launch_bounds__(kWave) void extend_f32_kernel(ExtendArgs a) {
         const float pt = expf(sc_s[j][t] - m_new);
         psum += pt;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pt, vb[(lane + e * kWave) * kBs + v_pos(t)], acc[e]);
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pt, vb[(lane + e * kWave) * bsz + v_pos(t)], acc[e]);
       }
       l_run[j] = l_run[j] * alpha + psum;
       m_run[j] = m_new;
@@ -757,7 +783,12 @@ int launch_e(const ExtendArgs& a, int32_t dtype, hipStream_t st) {
     const int64_t grid = (int64_t)kXcds * unit_groups * tiles;
     if (grid == 0) return 0;
     if (grid > 0x7fffffff) return -1;
-    extend_bf16_kernel<D, false><<<(unsigned)grid, NW * kWave, 0, st>>>(a, tiles, units);
+    if (a.block_size == 32)
+      extend_bf16_kernel<D, false, ExtendArgs, 32><<<(unsigned)grid, NW * kWave, 0, st>>>(a, tiles,
+                                                                                         units);
+    else
+      extend_bf16_kernel<D, false, ExtendArgs, 16><<<(unsigned)grid, NW * kWave, 0, st>>>(a, tiles,
+                                                                                         units);
   } else {
     if (a.max_q_len == 0) return 0;
     extend_f32_kernel<D><<<dim3(a.max_q_len, a.num_kv_heads, a.num_reqs), kWave, 0, st>>>(a);
@@ -775,7 +806,8 @@ int launch_p(const PrefixArgs& a, hipStream_t st) {
   const int64_t grid = (int64_t)kXcds * unit_groups * tiles;
   if (grid == 0) return 0;
   if (grid > 0x7fffffff || units > 0x7fffffff) return -1;
-  extend_bf16_kernel<D, true><<<(unsigned)grid, 8 * kWave, 0, st>>>(a, tiles, (int)units);
+  extend_bf16_kernel<D, true, PrefixArgs, 16><<<(unsigned)grid, 8 * kWave, 0, st>>>(a, tiles,
+                                                                                   (int)units);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

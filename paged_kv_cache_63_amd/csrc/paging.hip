@@ -302,13 +302,13 @@ __global__ __launch_bounds__(kThreads) void upload_append_kernel(
     uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int64_t bytes, int vec,
     int32_t up_wgs, const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
     const int32_t* __restrict__ slots, int64_t pieces, int32_t pieces_per_row, int32_t hkv,
-    int32_t d, int32_t num_blocks, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-    TableUpdates u) {
+    int32_t d, int32_t bs, int32_t num_blocks, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool, TableUpdates u) {
   if ((int32_t)blockIdx.x < up_wgs) {
     upload_bytes(dst, src, bytes, vec, blockIdx.x, up_wgs);
     apply_updates(u, blockIdx.x, up_wgs);
   } else
-    append_pieces<E>(k_new, v_new, slots, pieces, pieces_per_row, hkv, d, 16, num_blocks, k_pool,
+    append_pieces<E>(k_new, v_new, slots, pieces, pieces_per_row, hkv, d, bs, num_blocks, k_pool,
                      v_pool, blockIdx.x - up_wgs, gridDim.x - up_wgs);
 }
 
@@ -498,15 +498,15 @@ int launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t st, Tab
 
 int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slots_offset,
                          const void* k_new, const void* v_new, int32_t num_tokens, void* k_pool,
-                         void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d,
+                         void* v_pool, int32_t num_blocks, int32_t hkv, int32_t d, int32_t bs,
                          int32_t elem_bytes, hipStream_t st, TableUpdates u) {
   if (num_tokens == 0) return bytes > 0 || u.n > 0 ? launch_upload(dst, src, bytes, st, u) : 0;
-  if (num_tokens >= kBulkTokens) {
+  if (num_tokens >= kBulkTokens && bs == 16) {
     // bulk: the window scans read the slots many times, from the device copy
     int rc = bytes > 0 || u.n > 0 ? launch_upload(dst, src, bytes, st, u) : 0;
     if (rc) return rc;
     return launch_append(k_new, v_new, (const int32_t*)((const uint8_t*)dst + slots_offset),
-                         num_tokens, k_pool, v_pool, num_blocks, hkv, d, 16, elem_bytes, st);
+                         num_tokens, k_pool, v_pool, num_blocks, hkv, d, bs, elem_bytes, st);
   }
   const int vec = upload_vec(dst, src);
   const int64_t up = max(upload_grid(bytes, vec), min((u.n + kThreads - 1) / kThreads, (int64_t)1024));
@@ -517,12 +517,12 @@ int launch_upload_append(void* dst, const void* src, int64_t bytes, int64_t slot
   if (elem_bytes == 2)
     upload_append_kernel<2><<<(unsigned)g, kThreads, 0, st>>>(
         (uint8_t*)dst, (const uint8_t*)src, bytes, vec, (int32_t)up, (const uint8_t*)k_new,
-        (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, num_blocks, (uint8_t*)k_pool,
+        (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, bs, num_blocks, (uint8_t*)k_pool,
         (uint8_t*)v_pool, u);
   else
     upload_append_kernel<4><<<(unsigned)g, kThreads, 0, st>>>(
         (uint8_t*)dst, (const uint8_t*)src, bytes, vec, (int32_t)up, (const uint8_t*)k_new,
-        (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, num_blocks, (uint8_t*)k_pool,
+        (const uint8_t*)v_new, slots, pieces, ppr, hkv, d, bs, num_blocks, (uint8_t*)k_pool,
         (uint8_t*)v_pool, u);
   return status_of(hipGetLastError());
 }

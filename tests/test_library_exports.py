@@ -62,7 +62,8 @@ def test_workspace_size_formula(lib):
     assert ws(0, 8, 1, 64, 100, 64) == 0
 
 
-@pytest.mark.parametrize("dtype,hd,bs,code", [(7, 128, 16, -2), (1, 96, 16, -2), (1, 128, 32, -2)])
+@pytest.mark.parametrize("dtype,hd,bs,code", [(7, 128, 16, -2), (1, 96, 16, -2), (1, 128, 64, -2),
+                                              (1, 128, 8, -2)])
 def test_unsupported_combinations_rejected(lib, dtype, hd, bs, code):
     one = ctypes.c_void_p(8)
     rc = lib.paged_kv_append(one, one, one, 4, one, one, 10, 8, hd, bs, dtype, None)
