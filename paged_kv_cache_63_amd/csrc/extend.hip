@@ -22,9 +22,11 @@
 // phase (PV of the previous tile, then QK of the current one: 32 MFMAs fed
 // from LDS) and a vector phase (softmax of the current tile, plus the tile
 // copies, table lookups and the first LDS reads of the next matrix phase),
-// with a workgroup barrier after every phase, and waves 4..7 run one phase
-// behind waves 0..3.  So while one wave of a SIMD keeps its matrix core
-// busy, the other runs its exponentials on the vector ALU; the matrix
+// and waves 4..7 run one phase behind waves 0..3.  A workgroup barrier
+// follows every second phase (one per tile): between two barriers, waves
+// 0..3 run a matrix then a vector phase and waves 4..7 a vector then a
+// matrix phase.  So while one wave of a SIMD keeps its matrix core busy,
+// the other runs its exponentials on the vector ALU; the matrix
 // phase runs at raised issue priority so that the older wave's VALU work
 // cannot starve it.  The softmax uses no instruction that executes on the
 // matrix pipeline (bf16 dot products would wait for the other wave's
@@ -553,14 +555,19 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
   // j-1 and QK of tile j; vector phase t the softmax of tile t, the copy of
   // tile t+3 (tiles 0..2 are copied before the loop) and the table lookups
   // for tile t+4, whether or not this wave computes on those tiles (all
-  // eight waves share each copy).  Tile t occupies stage t % 5 from its copy
-  // until the PV in matrix phase t+1, which every wave has left before any
-  // wave starts vector phase t+2, the first that may refill the stage.
+  // eight waves share each copy).  A barrier ends every odd slot, so slots
+  // 2j and 2j+1 form one window: there waves 0..3 run matrix phase j and
+  // vector phase j, waves 4..7 vector phase j-1 and matrix phase j.  Tile t
+  // occupies stage t % 5 from its copy until the PV in matrix phase t+1
+  // (window t+1); the first copy that refills the stage is issued in vector
+  // phase t+2, which no wave starts before window t+2.
   //
   // Phase boundary after the phase in slot s.  Odd slots end where tile
-  // (s+1)/2 must be in LDS for everyone: this wave waits for its share,
-  // leaving in flight only the copies it issued after that tile (waves
-  // 0..3 have issued up to tile u+3 by then, waves 4..7 up to u+2).
+  // (s+1)/2 must be in LDS for everyone (matrix phase (s+1)/2 reads it in
+  // the next window): this wave waits for its share, leaving in flight only
+  // the copies it issued after that tile (waves 0..3 have issued up to tile
+  // u+3 by then, waves 4..7 up to u+2), and the barrier follows.  Even slots
+  // end without one.
   auto end_phase = [&](int s) {
     if (s & 1) {
       const int u = s >> 1;
@@ -568,8 +575,8 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
       if (n_out >= 2) wait_vm<2 * PER_T>();
       else if (n_out == 1) wait_vm<PER_T>();
       else wait_vm<0>();
+      wg_barrier();
     }
-    wg_barrier();
   };
   int e_nxt[NBW];   // table words of the next tile to copy
   auto copy_and_lookup = [&](int t) {
@@ -603,7 +610,6 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
   wait_vm<0>();
   wg_barrier();
   const int lag = lead ? 0 : 1;
-  if (!lead) wg_barrier();
   if (nt > 0) qk(0);
   int t = 0;
   const int t_plain = min(td, nt - 1);
@@ -637,7 +643,6 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     copy_and_lookup(t);
     end_phase(2 * t + 1 + lag);
   }
-  if (lead) wg_barrier();
 
   // Normalise and store: lane (row c32, group G) holds channels
   // dt*32 + 8*(v/4) + 4*G + v%4 of its row.
