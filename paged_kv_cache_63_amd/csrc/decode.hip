@@ -58,6 +58,68 @@ __device__ __forceinline__ int usable_len(const DecodeArgs& a, int s) {
   return L < cap_part ? L : cap_part;
 }
 
+
+// A wave-uniform value the compiler may hold in a vector register, moved to
+// a scalar one (inline-assembly "s" operands must be scalar registers).
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const uint8_t* uni(const uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  return (const uint8_t*)(((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v));
+}
+
+// Direct-to-LDS copies of one 16-token granule of one head into this wave's
+// LDS slot: dma_k moves the K rows (16 x D bf16, 32*D bytes at kbase),
+// dma_v the V half-rows (D channel rows of 16 tokens, 32 bytes each at
+// vbase + row * vrow_bytes).  Every instruction moves 1 KB: lane l writes
+// slot bytes i*1024 + 16*l and reads the global chunk that belongs there
+// (koff, voff per lane; the K chunk positions are XOR-swizzled by row, so
+// instruction i's lane offset is koff with the row-group bits flipped).
+// M0 is saved and restored; each s_nop covers the M0-write hazard.
+template <int D>
+__device__ __forceinline__ void dma_k(const uint8_t* kbase, uint32_t koff, uint32_t lds_k) {
+  constexpr int NI = D / 32;   // 1 KB instructions
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0" : "=s"(saved));
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t ko = koff ^ (uint32_t)((i * (1024 / (2 * D))) % (D / 8) * 16);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
+        :
+        : "s"(uni(lds_k + i * 1024)), "v"(ko), "s"(uni(kbase + i * 1024))
+        : "memory");
+  }
+  asm volatile("s_mov_b32 m0, %0" : : "s"(saved) : "memory");
+}
+template <int D>
+__device__ __forceinline__ void dma_v(const uint8_t* vbase, uint32_t voff, uint32_t lds_v,
+                                      uint32_t vrow_bytes) {
+  constexpr int NI = D / 32;
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0" : "=s"(saved));
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
+        :
+        : "s"(uni(lds_v + i * 1024)), "v"(voff), "s"(uni(vbase + i * 32 * vrow_bytes))
+        : "memory");
+  }
+  asm volatile("s_mov_b32 m0, %0" : : "s"(saved) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight;
+// also a compiler barrier, so that LDS reads of the copied data stay after it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------- bf16 decode
 // Balanced split: the work of the call is the list of (sequence, KV head,
 // block) triples, sequence-major; unit (s, h) owns nb(s) = ceil(L_s / 16)
@@ -82,9 +144,13 @@ __device__ __forceinline__ int usable_len(const DecodeArgs& a, int s) {
 // The query heads of the GQA group (g <= 16) fill the 16 columns, so one
 // read of a K/V block serves the whole group; the score tile comes out in
 // the register layout P^T needs, and the channel-major V rows make the V^T
-// operand one 8-byte load per lane.  K/V loads are non-temporal (each byte
-// is read once per call).  Block-table entries are fetched one per lane, 64
-// blocks per wave at a time, and broadcast with readlane.
+// operand one 8-byte read per lane.  Each wave stages its blocks in an LDS
+// slot of its own: direct-to-LDS copies bring block i+1's keys while the wave
+// computes on block i's (and its values once block i's have been read), so
+// a copy is in flight through most of the wave's compute without holding
+// registers.  The copies are non-temporal (each byte is read once per call).
+// Block-table entries are fetched one per lane, 64 blocks per wave at a
+// time, and broadcast with readlane.
 
 // Agent-coherent store / load of a piece's statistics.
 __device__ __forceinline__ void put(float* p, float v) {
@@ -230,6 +296,43 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   float* sm_l = sm_m + NW * 16;        // [NW][16]
   float* sm_x = sm_l + NW * 16;        // [NW][16] each wave's maximum
 
+  // Each wave's LDS slot for one granule: K rows [16][D] (16-byte chunk c
+  // of row r at position c ^ (r % (D/8))), then V channel rows [D][16]
+  // (the two 16-byte halves of row ch swapped where bit 3 of ch is set), so
+  // that the matrix-core operand reads hit distinct banks.  The slots alias
+  // the wave-merge area (a barrier separates the uses).
+  constexpr int ROWB = 2 * D;
+  constexpr int CPR = D / 8;
+  constexpr uint32_t SLOT = 64 * D;   // bytes: 32*D of K, 32*D of V
+  const char* slot_bytes = reinterpret_cast<const char*>(smem);
+  const uint32_t smem_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)smem;
+  const uint32_t lds_k = smem_lds + wave * SLOT;
+  const uint32_t lds_v = lds_k + 32 * D;
+  // Per-lane offsets, recomputed from the lane id where used (an opaque
+  // copy of the id keeps the compiler from holding them in registers across
+  // the block loop).
+  auto opaque_lane = [] {
+    uint32_t l = __lane_id();
+    asm volatile("" : "+v"(l));
+    return (int)l;
+  };
+  auto rk_off = [&](int l) {   // K fragment 0 of lane l
+    const int c = l & 15, gq = l >> 4;
+    return (uint32_t)(wave * SLOT + c * ROWB + ((gq ^ (c % CPR)) * 16));
+  };
+  auto rv_off = [&](int l) {   // V fragment 0 of lane l
+    const int c = l & 15, gq = l >> 4;
+    return (uint32_t)(wave * SLOT + 32 * D + c * 32 + (((gq & 1) ^ ((c >> 3) & 1)) * 16) + (gq >> 1) * 8);
+  };
+  auto dma_koff = [&](int l) {   // source of the slot bytes lane l copies in instruction 0
+    const int p = 16 * l;
+    const int r = p / ROWB, cp = (p % ROWB) / 16;
+    return (uint32_t)(r * ROWB + ((cp ^ (r % CPR)) * 16));
+  };
+  auto dma_voff = [&](int l) {
+    return (uint32_t)((l / 2) * (vrow * 2) + (((l & 1) ^ ((l >> 4) & 1)) * 16));
+  };
+
   // One piece: blocks [bb, be) of unit (s, h); piece k of np.
   auto piece = [&](int s, int h, int L, int bb, int be, int k, int np) {
     // Q^T operand: lane (head column col, group grp) holds 8 channels per product.
@@ -255,30 +358,53 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
 #pragma unroll
     for (int m = 0; m < KV; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // this wave's blocks: bb + wave + i*NW, i < cnt
+    // this wave's blocks: bb + wave + i*NW, i < cnt.  Each block's K and V
+    // granule is copied straight into the wave's LDS slot while the wave
+    // computes on the previous one, then read into registers.
     const int cnt = (be - bb - wave + NW - 1) / NW;
+    constexpr int NI = D / 32;   // copy instructions per K (or V) granule
+    auto kaddr = [&](int j, int phys) {
+      const int b = bb + wave + j * NW;
+      return (const uint8_t*)(kpool + ((int64_t)phys * hkv + h) * slab_elems +
+                              (b & ((1 << sh) - 1)) * head_elems);
+    };
+    auto vaddr = [&](int j, int phys) {
+      const int b = bb + wave + j * NW;
+      return (const uint8_t*)(vpool + ((int64_t)phys * hkv + h) * slab_elems +
+                              (b & ((1 << sh) - 1)) * kBs);
+    };
+    auto issue_k = [&](int j, int phys) { dma_k<D>(kaddr(j, phys), dma_koff(opaque_lane()), lds_k); };
+    auto issue_v = [&](int j, int phys) {
+      dma_v<D>(vaddr(j, phys), dma_voff(opaque_lane()), lds_v, (uint32_t)vrow * 2);
+    };
+    __syncthreads();   // the slots alias the previous piece's merge area
     for (int i0 = 0; i0 < cnt; i0 += kWave) {
       const int n_here = min(kWave, cnt - i0);
       int my_entry = 0;
       if (lane < n_here)
         my_entry = clamp_block(trow[(bb + wave + (i0 + lane) * NW) >> sh], a.num_blocks);
+      {
+        const int e0 = __builtin_amdgcn_readlane(my_entry, 0);
+        issue_k(i0, e0);
+        issue_v(i0, e0);
+      }
       for (int i = 0; i < n_here; ++i) {
         const int b = bb + wave + (i0 + i) * NW;
-        const int phys = __builtin_amdgcn_readlane(my_entry, i);
-        const int part = b & ((1 << sh) - 1);
-        const int64_t hb = ((int64_t)phys * hkv + h) * slab_elems;
-        const uint16_t* kr = kpool + hb + part * head_elems + col * D + grp * 8;   // token row = col
-        // channel row = col; tokens 4grp..4grp+3 sit at v_pos(4grp)
-        const uint16_t* vr = vpool + hb + col * vrow + part * kBs + v_pos(grp * 4);
+        const bool more = i + 1 < n_here;
+        const int e_next = __builtin_amdgcn_readlane(my_entry, more ? i + 1 : i);
+        // K of this block is in the slot (its V may still be in flight)
+        wait_vm<NI>();
         bf16x8 kd[KQ];
-        u32x2 vd[KV];
+        {
+          // (the per-product addresses are recomputed here rather than kept
+          // live across the loop)
+          const uint32_t rk = rk_off(opaque_lane());
 #pragma unroll
-        for (int kk = 0; kk < KQ; ++kk)
-          kd[kk] = __builtin_bit_cast(
-              bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + kk * 32)));
-#pragma unroll
-        for (int m = 0; m < KV; ++m)
-          vd[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vr + m * 16 * vrow));
+          for (int kk = 0; kk < KQ; ++kk)
+            kd[kk] = *reinterpret_cast<const bf16x8*>(slot_bytes + (rk ^ (uint32_t)(64 * kk)));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // K slot free
+        if (more) issue_k(i0 + i + 1, e_next);
         const int nvalid = L - b * kBs;   // tokens of this block inside the context
         f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -314,6 +440,15 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
           const u32x2 pw = __builtin_bit_cast(u32x2, pf);
           l_run += (bf16_lo(pw.x) + bf16_hi(pw.x)) + (bf16_lo(pw.y) + bf16_hi(pw.y));
         }
+        // V of this block is in the slot (the next block's K may be in flight)
+        if (more) wait_vm<NI>();
+        else wait_vm<0>();
+        u32x2 vd[KV];
+#pragma unroll
+        for (int m = 0; m < KV; ++m)
+          vd[m] = *reinterpret_cast<const u32x2*>(slot_bytes + rv_off(opaque_lane()) + m * 512);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // V slot free
+        if (more) issue_v(i0 + i + 1, e_next);
         if (partial) {
           // Tail tokens of a partly filled block hold arbitrary bits
           // (possibly NaN); p is 0 there but 0 * NaN is not, so clear those
@@ -787,7 +922,8 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     const size_t wave_area = (size_t)nw * g * D + 3 * nw * 16;
     const size_t merge_area = (size_t)2 * g * a.max_partitions + g;
     const size_t words = a.seq_prefix ? wave_area : max(wave_area, merge_area);
-    const size_t lds = words * sizeof(float);
+    // per-wave granule slots (K + V of 16 tokens), aliased with the merge areas
+    const size_t lds = max(words * sizeof(float), (size_t)nw * 64 * D);
     if (lds > kDecodeLdsMax) return -2;
     // (the shared-prefix entry runs only with 16-token blocks)
     auto kern = a.seq_prefix ? decode_bf16_kernel<D, NWS, true, 16>
