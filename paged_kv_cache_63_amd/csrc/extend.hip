@@ -30,10 +30,10 @@
 // phase runs at raised issue priority so that the older wave's VALU work
 // cannot starve it.  The softmax uses no instruction that executes on the
 // matrix pipeline (bf16 dot products would wait for the other wave's
-// MFMAs): row sums are taken by the matrix core itself, as products with an
-// all-ones operand.  The probabilities are pinned to the vector phase (the
-// compiler would otherwise sink them into the matrix phase that consumes
-// them).
+// MFMAs): row sums are taken by the matrix core itself, as small 4x4x4
+// products with an all-ones operand.  The probabilities are pinned to the
+// vector phase (the compiler would otherwise sink them into the matrix
+// phase that consumes them).
 //
 // LDS layouts (16-byte chunks; reads hit 64 distinct banks per 16 lanes):
 // K rows are XOR-swizzled (chunk c of row i at c ^ f(i)); each V channel
@@ -361,11 +361,11 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
 
   const float c2 = a.scale * kLog2e;   // scores -> base-2 exponent units
   float m_ref = -INFINITY;
-  f32x16 lsum;   // every value: the row sum of the lane's row
-#pragma unroll
-  for (int v = 0; v < 16; ++v) lsum[v] = 0.f;
-  const bf16x8 ones8 = bf16x8{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                              (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  // Row sums: each lane sums its own probabilities (every value of lsA and
+  // lsB holds the running sum of one half of the lane's keys); the two lanes
+  // of a row are added at the end.
+  f32x4 lsA = f32x4{0.f, 0.f, 0.f, 0.f}, lsB = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x4 ones4 = bf16x4{(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -395,12 +395,17 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     o[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / DT], o[i % DT], 0, 0, 0);
   };
   // Row sums of the rounded probabilities (exactly the weights PV uses) on
-  // the matrix core: with an all-ones A operand every row of the product is
-  // the sum over the block's keys.  The vector phase then needs no adds, and
-  // no bf16 dot instructions (those run on the matrix pipeline and would
-  // wait behind the other wave's MFMAs).
+  // the matrix core: v_mfma_f32_4x4x4_16b_bf16 with an all-ones A operand
+  // gives each lane the sum of its own four B values (16 blocks of 4x4: lane
+  // l supplies column l % 4 of block l / 4), issuing every ~9 cycles against
+  // 32 for a 32x32x16 product.  Two per 16-key sub-block, on two chains.
+  // The vector phase then needs no adds, and no bf16 dot instructions (those
+  // run on the matrix pipeline and would wait behind the other wave's MFMAs).
   auto sum_mfma = [&](int b) {
-    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pf[b], lsum, 0, 0, 0);
+    const bf16x4 lo = __builtin_shufflevector(pf[b], pf[b], 0, 1, 2, 3);
+    const bf16x4 hi = __builtin_shufflevector(pf[b], pf[b], 4, 5, 6, 7);
+    lsA = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones4, lo, lsA, 0, 0, 0);
+    lsB = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones4, hi, lsB, 0, 0, 0);
   };
   auto qk_mfma = [&](int i, bf16x8 f) {
     sc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i / 2], sc[i % 2], 0, 0, 0);
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NPRE + NSB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NPRE + 2 * NSB, 0);
     __builtin_amdgcn_s_setprio(0);
   };
   // QK alone (first tile): LA reads, then (MFMA, read) pairs.
@@ -495,7 +500,8 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
       // a row that has seen no key keeps m_ref = -inf: exp2(-inf - -inf) is
       // not 1, so rows that do not grow take alpha = 1 explicitly
       if constexpr (PREFIX) alpha = grow ? alpha : 1.f;
-      lsum *= alpha;
+      lsA *= alpha;
+      lsB *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m_ref = target;
@@ -646,7 +652,11 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
 
   // Normalise and store: lane (row c32, group G) holds channels
   // dt*32 + 8*(v/4) + 4*G + v%4 of its row.
-  const float l = lsum[0];
+  const float l = [&] {   // lanes l and l ^ 32 hold the two halves of the row's keys
+    const float part = lsA[0] + lsB[0];
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }();
   const int rr = wrow0 + c32;
   if (rr > last_row) return;
   if constexpr (PREFIX) {
