@@ -97,15 +97,17 @@ def _cpu_worker(seqs):
     from oracle import attention
     c = _CPU
     with threadpool_limits(1):
-        attention.decode(c["q"], c["kp"], c["vp"], c["tab"], c["lens"], c["scale"], 16, "bf16",
-                         seqs=seqs)
-    return len(seqs)
+        o = attention.decode(c["q"], c["kp"], c["vp"], c["tab"], c["lens"], c["scale"], 16, "bf16",
+                             seqs=seqs)
+    return seqs, o[seqs]
 
 
 def cpu_baseline(case, seconds):
     """The oracle (numpy float64) on the same decode workload, one process per
     host core, one BLAS thread each, each taking whole sequences.  Runs before
-    the GPU is touched (the pool of workers is forked)."""
+    the GPU is touched (the pool of workers is forked).  Returns the JSON
+    fields and the oracle's output rows of the workload's initial state (the
+    first pass), against which the GPU's decode of that state is checked."""
     import multiprocessing as mp
 
     from oracle import block_manager, paging
@@ -130,11 +132,15 @@ def cpu_baseline(case, seconds):
     S = case.num_seqs
     chunks = [list(range(i, S, cores)) for i in range(cores)]
     ctx = mp.get_context("fork")
+    ref = np.full((S, case.num_q_heads, case.head_dim), np.nan)
     with ctx.Pool(cores) as pool:
         t0 = time.perf_counter()
         steps = 0
         while True:
-            pool.map(_cpu_worker, chunks)
+            rows = pool.map(_cpu_worker, chunks)
+            if steps == 0:
+                for seqs, o in rows:
+                    ref[seqs] = o
             steps += 1
             el = time.perf_counter() - t0
             if el >= seconds or el / steps * (steps + 1) > 2.5 * seconds:
@@ -147,7 +153,7 @@ def cpu_baseline(case, seconds):
             "sample": f"{steps} full decode step(s) of the same workload ({S} sequences x "
                       f"{case.num_q_heads} heads, {int(np.sum(case.context_lens))} context "
                       f"tokens), {el:.1f} s on {cores} processes x 1 BLAS thread",
-            "gbps": round(steps * kv_bytes / el / 1e9, 4)}
+            "gbps": round(steps * kv_bytes / el / 1e9, 4)}, ref
 
 
 # ------------------------------------------------------------------ traffic
@@ -218,8 +224,10 @@ def bandwidth_ceilings(torch, lib, iters=10):
             "copy_gbps": round(2 * n / float(np.median(cpy)) / 1e9, 1)}
 
 
-def run_decode(args, case, torch, lib, alloc_cls):
-    """Decode loop over a plain (unshared) decode case."""
+def run_decode(args, case, torch, lib, alloc_cls, ref=None):
+    """Decode loop over a plain (unshared) decode case.  With ``ref`` (the
+    oracle's output rows for the initial state), the GPU's decode of that
+    state is compared with it first (max-abs error, every output)."""
     dev = torch.device("cuda:0")
     S, hq, hkv, d = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
     T = args.warmup + args.steps
@@ -260,6 +268,15 @@ def run_decode(args, case, torch, lib, alloc_cls):
     tables_d = torch.from_numpy(alloc.tables[:S]).to(dev)
     rows_s = np.arange(S)
     torch.cuda.synchronize()
+
+    parity = {}
+    if ref is not None:
+        lens0 = torch.from_numpy(np.asarray(case.context_lens, dtype=np.int32)).to(dev)
+        lib.paged_attention_decode(out, dev_words(case.q), k_pool, v_pool, tables_d, lens0,
+                                   int(case.context_lens.max()), case.scale, args.partition_size,
+                                   ws)
+        got = out.float().cpu().numpy().astype(np.float64)
+        parity = dict(max_abs_err=float(np.abs(got - ref).max()), parity_rows=int(S * hq))
 
     kv_per_tok = 2 * hkv * d * 2
     ev_pairs = []
@@ -324,7 +341,7 @@ def run_decode(args, case, torch, lib, alloc_cls):
                bytes=[call_bytes(ln) for ln in lens_sampled],
                step_bytes=[call_bytes(ln) for ln in lens_seen],
                flush_durs=flush, flush_bytes=call_bytes(lens_seen[-1]),
-               ctx_mean=float(alloc.lens[:S].mean()))
+               ctx_mean=float(alloc.lens[:S].mean()), **parity)
     if getattr(args, "keep_state", False):     # for tests of this loop: what the last step saw
         res["state"] = dict(out=out, q=q_steps[T - 1], k_new=k_steps[T - 1], v_new=v_steps[T - 1],
                             k_pool=k_pool, v_pool=v_pool, tables=alloc.tables[:S].copy(),
@@ -736,9 +753,9 @@ def main():
     if args.workload == "long-context-decode" and args.partition_size == 0:
         args.partition_size = 512          # the long-context workload's stated split
     case = make_case(args.workload, T)
-    cpu = None
+    cpu, ref = None, None
     if not args.no_cpu_baseline and args.workload in ("gqa4-decode",):
-        cpu = cpu_baseline(case, args.cpu_seconds)
+        cpu, ref = cpu_baseline(case, args.cpu_seconds)
 
     import torch
     from paged_kv_cache_63_amd import BlockAllocator
@@ -785,8 +802,13 @@ def main():
         r = run_shared(args, case, torch, lib, BlockAllocator)
         kern = ["decode.hip"] if args.plain_decode else ["decode.hip", "extend.hip"]
     else:
-        r = run_decode(args, case, torch, lib, BlockAllocator)
+        r = run_decode(args, case, torch, lib, BlockAllocator, ref=ref)
         kern = ["decode.hip"]
+        if cpu is not None and "max_abs_err" in r:
+            cpu["parity"] = {"max_abs_err": r["max_abs_err"], "tolerance": 2e-2,
+                             "rows": r["parity_rows"],
+                             "what": "GPU decode of the workload's initial state against these "
+                                     "oracle rows, every output"}
 
     el = r["elapsed"]
     ms_step = el / args.steps * 1e3
