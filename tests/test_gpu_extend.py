@@ -22,10 +22,12 @@ class LibExtendState:
 
     def __init__(self, e, free_order=None):
         R = len(e.prefix_lens)
-        mb = int(max(-(-int(x) // 16) for x in e.seq_lens))
-        self.alloc = BlockAllocator(e.num_blocks, 16, max_seqs=R, max_blocks_per_seq=mb,
+        bs = e.block_size
+        mb = int(max(-(-int(x) // bs) for x in e.seq_lens))
+        self.alloc = BlockAllocator(e.num_blocks, bs, max_seqs=R, max_blocks_per_seq=mb,
                                     free_order=e.free_order if free_order is None else free_order)
-        self.k_pool, self.v_pool = poisoned_pools(e.num_blocks, e.num_kv_heads, e.head_dim, e.dtype)
+        self.k_pool, self.v_pool = poisoned_pools(e.num_blocks, e.num_kv_heads, e.head_dim, e.dtype,
+                                                  bs=bs)
         sids = [self.alloc.new_seq() for _ in range(R)]
         pslots = np.concatenate([self.alloc.append_tokens(s, int(p))[0]
                                  for s, p in zip(sids, e.prefix_lens)])
@@ -165,4 +167,72 @@ def test_large_logits(gpu, factor):
     assert np.isfinite(out).all()
     err = np.abs(out - want).max()
     print(f"large logits x{factor}: max |err| {err:.3e}")
+    assert err <= 2e-2, err
+
+
+# Many workgroups.  The bf16 kernel runs one workgroup per (request, KV
+# head, 256-row tile); the (request, KV head) units x, x + 8, ... share XCD
+# x.  The cases below give every XCD several times more workgroups than it
+# has compute units, of very different lengths, including empty ones.
+
+
+def _extend_checked(e, reqs=None):
+    """Pool bits, then the extend output against the oracle (all requests,
+    or the listed ones); returns the max error."""
+    st = LibExtendState(e)
+    out = st.extend()
+    kp, vp, tab, _, nslots = P.extend_state(e)
+    assert np.array_equal(st.new_slots, nslots)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_of(st.k_pool), kp) and np.array_equal(words_of(st.v_pool), vp)
+    assert bool(torch.isfinite(out.float()).all())
+    want = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tab, e.scale, e.block_size,
+                            "bf16", reqs=reqs)
+    rows = np.concatenate([np.arange(int(e.cu_new[r]), int(e.cu_new[r + 1]))
+                           for r in (range(len(e.new_lens)) if reqs is None else reqs)])
+    if not len(rows):
+        return 0.0
+    got = f64_of(out[torch.from_numpy(rows).to(out.device)])
+    return float(np.abs(got - want[rows]).max())
+
+
+@pytest.mark.parametrize("bs,hq,hkv,d", [(16, 32, 8, 128), (16, 32, 8, 64), (32, 32, 8, 128),
+                                         (16, 8, 2, 128)])
+def test_many_ragged_requests(gpu, bs, hq, hkv, d):
+    """Ragged requests (some with no new token, some with one, chunks that
+    end inside a row tile and inside a key block, cached prefixes from none
+    to ~900 tokens), 120 workgroups per XCD: every output against the
+    oracle."""
+    R = 24 if hkv == 8 else 96
+    rng = np.random.default_rng(4100 + bs + d + hkv)
+    new = rng.integers(1, 300, size=R, endpoint=True)
+    new[[0, 5, 11]] = 0
+    new[[1, 7]] = 1
+    new[2] = 300
+    e = extend_case(4100 + bs + d + hkv, R, 0, 900, 0, 0, hq, hkv, d, "bf16", block_size=bs,
+                    new_lens=new)
+    g = hq // hkv
+    items = -(-R * hkv // 8) * -(-300 * g // 256)
+    assert 32 < items <= 1024
+    err = _extend_checked(e)
+    print(f"ragged bs={bs} d={d} hq={hq} hkv={hkv} workgroups/XCD={items}: max |err| {err:.3e}")
+    assert err <= 2e-2, err
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("R", [128, 129])
+def test_large_batches(gpu, R):
+    """128 and 129 requests x 8 KV heads x 8 row tiles (1024 and 1032
+    workgroups per XCD, the first request 512 new tokens long, the others
+    1..512): every output finite, the pool bit for bit, and nine requests
+    spread over the batch against the oracle."""
+    rng = np.random.default_rng(4200 + R)
+    new = rng.integers(1, 512, size=R, endpoint=True)
+    new[0] = 512
+    e = extend_case(4200 + R, R, 0, 96, 0, 0, 32, 8, 128, "bf16", new_lens=new)
+    items = -(-R * 8 // 8) * 8
+    assert items == (1024 if R == 128 else 1032)
+    reqs = sorted({0, 1, R // 4, R // 2, R // 2 + 1, 3 * R // 4, R - 3, R - 2, R - 1})
+    err = _extend_checked(e, reqs=reqs)
+    print(f"R={R} ({items} workgroups/XCD): max |err| over {len(reqs)} requests {err:.3e}")
     assert err <= 2e-2, err
