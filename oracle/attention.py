@@ -131,6 +131,9 @@ def extend(q_words, cu_seqlens_q, seq_lens, k_pool, v_pool, block_tables,
     Guide", "RadixAttention Architecture", steps of the longest-prefix search:
     only the unmatched suffix is prefilled over the reused pages).
 
+    A request with no new token owns no row of the output, whatever its
+    prefix, so it is passed over.
+
     q_words: ``[Tq][Hq][D]`` raw words.  Returns ``[Tq][Hq][D]`` float64
     (rows outside ``reqs``/``heads`` are NaN).
     """
@@ -141,6 +144,8 @@ def extend(q_words, cu_seqlens_q, seq_lens, k_pool, v_pool, block_tables,
     for r in (range(R) if reqs is None else reqs):
         q0, q1 = int(cu_seqlens_q[r]), int(cu_seqlens_q[r + 1])
         n = q1 - q0
+        if n == 0:
+            continue                                        # no new token, no output row
         L = int(seq_lens[r])
         prefix = L - n
         k, v = _gathered(k_pool, v_pool, block_tables[r], L, block_size, dtype)

@@ -183,6 +183,35 @@ def test_extend_equals_decode_per_token(dtype):
     assert P.err_extend_vs_decode(e) < 1e-13
 
 
+def test_extend_empty_requests_change_nothing():
+    """Requests with no new token (one with no prefix either, one with a
+    cached prefix) own no output row: the other requests' rows equal those
+    of the same batch without them, and each row equals the one-request
+    batch that holds only its own request (requests are independent)."""
+    e = extend_case(73, 4, 0, 0, 0, 0, 4, 2, 16, "fp32",
+                    prefix_lens=[0, 30, 0, 17], new_lens=[0, 9, 5, 0])
+    kp, vp, tab, _, _ = P.extend_state(e)
+    got = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tab, e.scale, 16, "fp32")
+    assert got.shape[0] == 14 and np.isfinite(got).all()
+    for r in (1, 2):
+        a, b = int(e.cu_new[r]), int(e.cu_new[r + 1])
+        one = attention.extend(e.q[a:b], np.array([0, b - a]), e.seq_lens[r:r + 1],
+                               kp, vp, tab[r:r + 1], e.scale, 16, "fp32")
+        assert np.array_equal(got[a:b], one)
+    # the second request against a direct softmax over its 39 contiguous
+    # tokens taken from the generator (30 cached, then 9 new), not the pool
+    k = np.concatenate([P.torch_widen(e.prefix_k[0:30], "fp32").numpy(),
+                        P.torch_widen(e.new_k[0:9], "fp32").numpy()])
+    v = np.concatenate([P.torch_widen(e.prefix_v[0:30], "fp32").numpy(),
+                        P.torch_widen(e.new_v[0:9], "fp32").numpy()])
+    q = P.torch_widen(e.q[0:9], "fp32").numpy()
+    for i in range(9):
+        for j in range(4):
+            z = e.scale * (k[:31 + i, j // 2] @ q[i, j])
+            w = np.exp(z - z.max())
+            assert np.abs(got[i, j] - w @ v[:31 + i, j // 2] / w.sum()).max() < 1e-12
+
+
 def test_extend_zero_prefix_is_causal_self_attention():
     """No cached prefix: extend is plain causal self-attention, checked
     against torch SDPA with is_causal=True on the contiguous new tokens."""
