@@ -171,7 +171,9 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *   context_lens   [num_seqs] int32, tokens in each context (the decoded
  *                  token's own key/value included); 0 gives a zero row
  *   max_context_len  host-side upper bound of context_lens (sizes the
- *                  workspace; contexts longer than it are cut to it)
+ *                  workspace).  A precondition: a longer context is cut to
+ *                  the (P - 1) x partition_size tokens the workspace can
+ *                  hold (P below), never read past it
  *   scale          softmax scale applied to q.k
  *   partition_size the smallest piece of a context computed on its own
  *                  (tokens, a multiple of block_size; 0 = 512).  bf16: the
@@ -349,6 +351,7 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
  *
  *   out, q         [total_q][num_q_heads][head_dim]  (dtype)
  *   cu_seqlens_q   [num_reqs+1] int32: request r owns rows cu[r] .. cu[r+1]-1
+ *                  (none when it has no new token, whatever its prefix)
  *   seq_lens       [num_reqs] int32: prefix + new tokens of request r; the
  *                  new tokens' keys/values must already be in the pool
  *   max_q_len      host-side bound of cu[r+1]-cu[r]   (sizes the grid)
