@@ -209,6 +209,29 @@ def test_context_longer_than_declared_max_is_cut_not_overrun(gpu):
     assert np.abs(f64_of(out) - want).max() <= 2e-2
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,d,ptok", [("bf16", 32, 8, 128, 0), ("bf16", 32, 8, 128, 16),
+                                                  ("bf16", 16, 1, 64, 0), ("fp32", 8, 2, 64, 0)])
+def test_many_short_sequences(gpu, dtype, hq, hkv, d, ptok):
+    """3000 sequences of 0 to 119 tokens (a tenth empty, a tenth of one
+    token): the plan scans the batch in several rounds, a range holds dozens
+    of whole (sequence, KV head) units, and every output is compared.  With
+    one or two tokens an output is nearly one value row, so the bf16 rounding
+    of the output alone reaches 2^-6 for values in [4, 8): ~1e-2 here."""
+    rng = np.random.default_rng(9500 + hq + d + ptok)
+    S = 3000
+    lens = rng.integers(0, 120, size=S)
+    lens[rng.random(S) < 0.1] = 0
+    lens[rng.random(S) < 0.1] = 1
+    case = decode_case(9501 + hq + d + ptok, S, 0, 0, hq, hkv, d, dtype, lens=lens)
+    st = LibDecodeState(case)
+    out, _ = st.decode(partition_size=ptok)
+    got = f64_of(out)
+    assert np.array_equal(got[lens == 0], np.zeros_like(got[lens == 0]))
+    err = np.abs(got - _oracle_out(case)).max()
+    print(f"S={S} {dtype} hq={hq} hkv={hkv} d={d} ptok={ptok}: max |err| {err:.3e}")
+    assert err <= TOL[dtype], err
+
+
 @pytest.mark.parametrize("fill", ["5a", "ff", "00", "random"])
 def test_workspace_reused_across_calls(gpu, fill):
     """One workspace (filled with garbage first) serves consecutive calls of
