@@ -181,24 +181,27 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *                  are dealt in equal contiguous ranges of
  *                  C = max(partition_size / block_size, ceil(total / W))
  *                  blocks to W = 2 x (compute units) workgroups; a (sequence,
- *                  KV head) that meets several ranges is computed in pieces
- *                  and merged by the piece that finishes last.  fp32: fixed
- *                  partitions of partition_size tokens, then a merge pass.
+ *                  KV head) that meets several ranges is computed in pieces,
+ *                  which a second kernel on the same stream merges.  fp32:
+ *                  fixed partitions of partition_size tokens, then a merge
+ *                  pass.
  *   workspace      device memory of at least
  *                  paged_attention_decode_workspace_size(...) bytes, 8-byte
  *                  aligned, owned by the caller, any contents (no clearing
- *                  is needed between calls; see arrive below).  Layout,
+ *                  is needed between calls; see count below).  Layout,
  *                  P = ceil(max_context_len / partition_size) + 1 pieces
  *                  per context:
  *                    o_part [num_seqs][num_q_heads][P][head_dim]  fp32, a
  *                                                  piece's normalised output
  *                    m_part [num_seqs][num_q_heads][P]  fp32, max scaled score
  *                    l_part [num_seqs][num_q_heads][P]  fp32, sum exp(score - m)
- *                    arrive [num_seqs][num_kv_heads]  uint64: bits 24..63
- *                                  a per-call tag, bits 0..23 the pieces of
- *                                  that call arrived.  A word with another
- *                                  call's tag counts as no arrival, so old
- *                                  contents are harmless; arbitrary contents
+ *                    count  [num_seqs][num_kv_heads]  uint64, written for
+ *                                  a (sequence, KV head) computed in several
+ *                                  pieces: bits 24..63 a per-call tag, bits
+ *                                  0..23 its piece count.  A word with
+ *                                  another call's tag counts as one piece
+ *                                  (nothing to merge), so old contents are
+ *                                  harmless; arbitrary contents
  *                                  are misread only if a word holds exactly
  *                                  the call's 40-bit tag (tags run in one
  *                                  process-wide sequence from a random start
@@ -233,7 +236,7 @@ int paged_attention_decode(void* out, const void* q,
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
  * result as paged_attention_decode, without the workspace arguments: the
- * call's pieces and arrival words live in a fixed array the library holds
+ * call's pieces and piece-count words live in a fixed array the library holds
  * on every GPU it runs on (64 MiB, kept until the process ends).  The call
  * allocates nothing.
  *
@@ -247,7 +250,7 @@ int paged_attention_decode(void* out, const void* q,
  * contents: calls in order on one stream are fine, but calls that overlap in
  * time on one GPU (other streams, other host threads) race and give wrong
  * results.  The first call on a GPU also enqueues, on `stream`, a small
- * kernel that clears the array's arrival words.
+ * kernel that clears the array's piece-count words.
  */
 int paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
                                    const void* v_pool, int32_t num_blocks,
@@ -308,7 +311,7 @@ size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t nu
  *                  [num_seqs][num_q_heads][NS][head_dim], m and l
  *                  [num_seqs][num_q_heads][NS] fp32 (NS key splits).  Every
  *                  64-bit word carries the writing call's tag in bits 24..63,
- *                  as paged_attention_decode's arrival words do, and a word
+ *                  as paged_attention_decode's piece-count words do, and a word
  *                  with another tag reads as zero: nothing is cleared
  *                  between calls, and the same guarantee holds (a workspace
  *                  zero-filled at allocation is never misread).

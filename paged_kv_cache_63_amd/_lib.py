@@ -266,7 +266,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
         raise ValueError("block_tables [S][max_blocks], context_lens [S]")
     need = paged_attention_decode_workspace_size(S, hq, hkv, d, max_context_len, partition_size)
     if need and workspace is None:
-        # zero-filled once: no arrival word can then hold a call's tag by chance
+        # zero-filled once: no piece-count word can then hold a call's tag by chance
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _dev(workspace)
@@ -327,7 +327,7 @@ def paged_attention_decode_shared(out, q, k_pool, v_pool, block_tables, context_
     need = paged_attention_decode_shared_workspace_size(S, hq, hkv, d, max_context_len,
                                                         partition_size, G, max_size, max_pb)
     if need and workspace is None:
-        # zero-filled: no arrival word or per-sequence word then holds a tag
+        # zero-filled: no piece-count word or per-sequence word then holds a tag
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _dev(workspace)

@@ -103,8 +103,8 @@ PrefixSplit prefix_split(int32_t num_groups, int32_t max_group_size, int32_t max
   return {(int32_t)blocks, (int32_t)((max_prefix_blocks + blocks - 1) / blocks)};
 }
 
-// A tag per decode call for its arrival words (bits 24..63 of a word;
-// the count of the call's arrived pieces sits below).  Tags come from one
+// A tag per decode call for its tagged words (bits 24..63 of a word; a
+// count sits below: a split unit's pieces).  Tags come from one
 // process-wide sequence that starts at a random point with its top bit set:
 // a word written by an earlier call carries an earlier tag, and a word the
 // library never wrote matches only if it happens to hold this exact tag.
@@ -123,7 +123,7 @@ struct SharedLayout {
 };
 SharedLayout shared_layout(int64_t S, int64_t hq, int64_t hkv, int64_t D, int64_t P, int64_t NS) {
   SharedLayout l{};
-  // the plain decode's layout (pieces, then arrival words), then one tagged
+  // the plain decode's layout (pieces, then piece-count words), then one tagged
   // word per sequence (8-byte aligned: D + 2 is even)
   const size_t dec = (size_t)S * hq * P * (D + 2) * 4 + (size_t)S * hkv * 8;
   l.seq_prefix = dec;

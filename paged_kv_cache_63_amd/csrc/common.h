@@ -83,9 +83,11 @@ struct DecodeArgs {
   float* part_o;   // [S][Hq][P][D]
   float* part_m;   // [S][Hq][P]
   float* part_l;   // [S][Hq][P]
-  // [S][Hkv] arrival words, bits 24..63 a call's tag and bits 0..23 the
-  // pieces of that call arrived so far; a word with another tag counts as
-  // zero, so the words need no clearing between calls.
+  // [S][Hkv] piece-count words: a unit computed in several pieces gets,
+  // from its first piece, bits 24..63 the call's tag and bits 0..23 its
+  // piece count, which the fold reads; a word with another tag counts as
+  // zero (the unit was finished in one piece), so the words need no
+  // clearing between calls.
   uint64_t* arrive;
   uint64_t tag;       // this call's tag, already in bits 24..63
   int32_t num_blocks;
@@ -116,12 +118,12 @@ int launch_decode(const DecodeArgs& a, int32_t dtype, hipStream_t st);
 
 // The decode workspace the allocation-free entry uses: one fixed device
 // array per GPU, kScratchBytes long, whose first kScratchArriveBytes hold the
-// arrival words (one per (sequence, KV head), so at most
+// piece-count words (one per (sequence, KV head), so at most
 // kScratchArriveBytes / 8 units) and the rest the pieces' partials.
 constexpr size_t kScratchBytes = size_t(64) << 20;
 constexpr size_t kScratchArriveBytes = size_t(256) << 10;
 // Device address of the current device's array; the first call on a device
-// looks it up and clears its arrival words with a kernel on st.  0 or a
+// looks it up and clears its piece-count words with a kernel on st.  0 or a
 // PKV_ERR_* code.
 int decode_scratch(hipStream_t st, uint8_t** base);
 

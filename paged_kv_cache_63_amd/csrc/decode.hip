@@ -1,13 +1,13 @@
 // Paged decode attention for gfx950: one query token per sequence against
 // its whole paged context.
 //
-// bf16: one kernel.  The call's K/V blocks are dealt out in equal contiguous
-// ranges to a fixed grid of workgroups; a (sequence, KV head) unit that
-// straddles ranges is computed in pieces and merged by its last piece
-// (log-sum-exp rule), so the merge needs no second launch.
+// bf16: the call's K/V blocks are dealt out in equal contiguous ranges to a
+// fixed grid of workgroups; a (sequence, KV head) unit that straddles
+// ranges is computed in pieces, each leaving a partial, and a small second
+// kernel (the fold) merges every split unit's pieces by the log-sum-exp rule.
 // Shared-prefix variant (bf16): each sequence's pass starts after the blocks
-// a prefix pass has already covered, every piece leaves a partial, and a
-// small kernel then merges each unit's pieces with the prefix partials.
+// a prefix pass has already covered, every piece leaves a partial, and the
+// fold merges each unit's pieces with the prefix partials.
 // fp32: a plain vector-ALU pass over fixed partitions (one wave per
 // workgroup, exact expf), then a merge pass for contexts with more than one
 // partition: out = sum_p o_p l_p e^(m_p-M) / sum_p l_p e^(m_p-M).
@@ -132,8 +132,11 @@ __device__ __forceinline__ void wait_vm() {
 // fixed-size partitions leaves compute units idle while ragged sequences
 // finish).  A unit that falls into one workgroup's range is finished there;
 // a unit split over several ranges is computed in pieces, each piece
-// writes its (o, m, l) to the workspace, and the piece that completes last
-// (an atomic arrival count per unit) merges them by the log-sum-exp rule.
+// writes its (o, m, l) to the workspace, and the fold kernel merges them by
+// the log-sum-exp rule once the call's pieces are all written (a merge
+// inside this launch, by the piece that arrived last, left every
+// workgroup's last piece waiting for its stores, an atomic count and the
+// merge's loads at the end of the kernel).
 //
 // Per piece the NW waves take blocks b, b+NW, ... of the piece; per 16-token
 // block a wave issues two matrix-core products:
@@ -151,14 +154,6 @@ __device__ __forceinline__ void wait_vm() {
 // registers.  The copies are non-temporal (each byte is read once per call).
 // Block-table entries are fetched one per lane, 64 blocks per wave at a
 // time, and broadcast with readlane.
-
-// Agent-coherent store / load of a piece's statistics.
-__device__ __forceinline__ void put(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Sum over the workgroup (all threads get the result); uses red[NW].
 template <int NW>
@@ -204,7 +199,6 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   __shared__ int red[NW];
   __shared__ int sh_first_g;
   __shared__ int sh_first_s;
-  __shared__ int sh_lastv[2];
   constexpr int KQ = D / 32;  // QK products per block
   constexpr int KV = D / 16;  // PV products per block
   constexpr int NT = NW * kWave;
@@ -499,78 +493,26 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
         acc += sm_o[(v * g + c) * D + dd] * f;
       }
       const int64_t row = (int64_t)s * hq + h * g + c;
-      if constexpr (SHARED) {
-        // every piece is a partial; a later kernel merges them with the
-        // prefix pass's partials
-        a.part_o[(row * P + k) * D + dd] = acc / lsum;
-        if (dd == 0) {
-          a.part_m[row * P + k] = M * kLn2;
-          a.part_l[row * P + k] = lsum;
-        }
-      } else if (np == 1) {
+      if (!SHARED && np == 1) {
         out[row * D + dd] = f32_to_bf16(acc / lsum);
       } else {
-        put(&a.part_o[(row * P + k) * D + dd], acc / lsum);
+        // a partial for the fold (in the shared-prefix variant every piece
+        // is one: the fold adds the prefix pass's partials)
+        a.part_o[(row * P + k) * D + dd] = acc / lsum;
         if (dd == 0) {
-          put(&a.part_m[row * P + k], M * kLn2);  // natural-log units
-          put(&a.part_l[row * P + k], lsum);
+          a.part_m[row * P + k] = M * kLn2;  // natural-log units
+          a.part_l[row * P + k] = lsum;
         }
       }
     }
-    if constexpr (SHARED)   // pieces of the unit, for the fold kernel
-      if (k == 0 && tid == 0) a.arrive[(int64_t)s * hkv + h] = a.tag | (uint64_t)np;
-  };
-
-  // Merge all np pieces of unit (s, h) (called by the piece that arrived
-  // last): the pieces' weights l_j e^(m_j - M) go through LDS (one load per
-  // (head, piece) across the workgroup), then every (head, channel) thread
-  // sums its o_j with eight loads in flight.
-  auto merge = [&](int s, int h, int np) {
-    float* sw = smem;   // [g][np] m, [g][np] weights, [g] inverse sums
-    for (int idx = tid; idx < g * np; idx += NT) {
-      const int c = idx / np;
-      const int j = idx - c * np;
-      const int64_t row = (int64_t)s * hq + h * g + c;
-      sw[idx] = get(&a.part_m[row * P + j]);
-      sw[g * np + idx] = get(&a.part_l[row * P + j]);
-    }
-    __syncthreads();
-    if (tid < g) {
-      float M = -INFINITY;
-      for (int j = 0; j < np; ++j) M = fmaxf(M, sw[tid * np + j]);
-      float wsum = 0.f;
-      for (int j = 0; j < np; ++j) {
-        const float wt = sw[g * np + tid * np + j] * expf(sw[tid * np + j] - M);
-        sw[g * np + tid * np + j] = wt;
-        wsum += wt;
-      }
-      sw[2 * g * np + tid] = 1.f / wsum;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < g * D; idx += NT) {
-      const int c = idx / D;
-      const int dd = idx - c * D;
-      const int64_t row = (int64_t)s * hq + h * g + c;
-      const float* wts = sw + g * np + c * np;
-      float acc = 0.f;
-      for (int j0 = 0; j0 < np; j0 += 8) {
-        float ov[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ov[u] = get(&a.part_o[(row * P + min(j0 + u, np - 1)) * D + dd]);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (j0 + u < np) acc = fmaf(wts[j0 + u], ov[u], acc);
-      }
-      out[row * D + dd] = f32_to_bf16(acc * sw[2 * g * np + c]);
-    }
-    __syncthreads();   // the LDS is reused by the next merge
+    // the unit's piece count, for the fold (kernel order makes the pieces
+    // visible to it)
+    if (k == 0 && (SHARED || np > 1) && tid == 0)
+      a.arrive[(int64_t)s * hkv + h] = a.tag | (uint64_t)np;
   };
 
   // Walk the units that intersect [lo, hi).  Only the first and the last
-  // of them can be split (the others lie wholly inside the range), so at
-  // most two pieces wait to be published.
-  int n_pend = 0;
-  int pend_s[2] = {0, 0}, pend_h[2] = {0, 0}, pend_np[2] = {0, 0};
+  // of them can be split (the others lie wholly inside the range).
   while (G < hi && s < S) {
     const int L = usable_len(a, s);
     const int nb_all = (L + kBs - 1) / kBs;
@@ -589,65 +531,11 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
           np = (int)((uint32_t)(Gh + nb - 1) / (uint32_t)C) - first + 1;
         }
         piece(s, h, L, st + (int)(a0 - Gh), st + (int)(a1 - Gh), k, np);
-        if (!SHARED && np > 1 && n_pend < 2) {
-          pend_s[n_pend] = s;
-          pend_h[n_pend] = h;
-          pend_np[n_pend] = np;
-          ++n_pend;
-        }
       }
     }
     G += hkv * nb;
     ++s;
   }
-  if (n_pend == 0) return;
-
-  // Publish this workgroup's split pieces (once, at the end, so that the
-  // stores have long completed); the piece of a unit that arrives last
-  // merges the unit.
-  //
-  // Memory ordering.  The pieces' o, m and l travel between workgroups that
-  // may sit on different XCDs, whose L2 caches are not coherent with one
-  // another.  They are not ordered by a release/acquire pair (in HIP's
-  // model that is a fence: on gfx950 an agent-scope release writes back
-  // and an acquire invalidates this XCD's whole L2, which made the kernel
-  // about 4x slower).  Instead every access to them is an agent-scope
-  // atomic (put/get: relaxed, compiled to sc1 stores that write through
-  // the L2 and sc1 loads that read past it), and the order comes from the
-  // hardware:
-  //   1. `s_waitcnt vmcnt(0)` below returns only when each of this thread's
-  //      write-through stores has been acknowledged by the memory side,
-  //      where every XCD's agent-scope accesses meet;
-  //   2. the barrier then holds every thread until all have passed step 1,
-  //      so all of the workgroup's piece data is at the memory side before
-  //      thread tid < n_pend counts the piece in;
-  //   3. the count is an agent-scope compare-and-swap, performed at that
-  //      same memory side, so the workgroup that reads the final count has
-  //      seen every earlier count and hence every earlier piece's stores;
-  //   4. that workgroup's merge reads the pieces with sc1 loads, which do
-  //      not return stale lines from its own L2.
-  // This leans on gfx950's cache behaviour rather than on the language's
-  // memory model, and holds only with the accesses kept as they are.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid < n_pend) {
-    // count this piece in: a word that carries another call's tag holds
-    // no arrival of this call
-    uint64_t* w = &a.arrive[(int64_t)pend_s[tid] * hkv + pend_h[tid]];
-    constexpr uint64_t kCount = kTagLow;
-    uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t prev;
-    while (true) {
-      prev = (old & ~kCount) == a.tag ? (old & kCount) : 0;
-      if (__hip_atomic_compare_exchange_strong(w, &old, a.tag | (prev + 1), __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
-    sh_lastv[tid] = prev == (uint64_t)(pend_np[tid] - 1);
-  }
-  __syncthreads();
-  for (int i = 0; i < n_pend; ++i)
-    if (sh_lastv[i]) merge(pend_s[i], pend_h[i], pend_np[i]);
 }
 
 // ---------------------------------------------------------------- fp32 pass 1
@@ -832,13 +720,14 @@ int raise_lds_limit(const void* kern, std::atomic<uint64_t>* done) {
   return 0;
 }
 
-// Shared-prefix decode, last step: for every (sequence, KV head) the pieces
-// of the sequence's own pass and the prefix pass's partials are combined by
-// the log-sum-exp rule, out = sum_j o_j l_j e^(m_j - M) / sum_j l_j e^(m_j - M)
-// (natural-log statistics).  The unit's piece count and the sequence's
-// prefix-partial count come from words tagged by this call's kernels; a
-// word with another tag means 0 (a unit with an empty context, which the
-// decode kernel gave its zero rows, or a sequence in no group).
+// Fold, the bf16 decode's last step: for every (sequence, KV head) whose
+// context was split, its pieces (and, in the shared-prefix decode, the
+// prefix pass's partials) are combined by the log-sum-exp rule,
+// out = sum_j o_j l_j e^(m_j - M) / sum_j l_j e^(m_j - M) (natural-log
+// statistics).  The unit's piece count and the sequence's prefix-partial
+// count come from words tagged by this call's kernels; a word with another
+// tag means 0 (a unit the decode kernel finished in one piece or gave its
+// zero rows, or a sequence in no group).
 template <int D>
 __global__ __launch_bounds__(256) void decode_fold_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) float fold_s[];   // [g][n] m, [g][n] weights, [g] 1/sum
@@ -853,10 +742,42 @@ __global__ __launch_bounds__(256) void decode_fold_kernel(DecodeArgs a) {
   if (np <= 0) return;
   const int NS = a.num_splits;
   const int P = a.max_partitions;
-  const uint64_t pw = a.seq_prefix[s];
+  const uint64_t pw = a.seq_prefix ? a.seq_prefix[s] : 0;
   const int nsp = (pw & ~kTagLow) == a.tag ? min((int)((pw >> 20) & 0xf), NS) : 0;
   const int n = np + nsp;
   const int tid = threadIdx.x;
+  if (nsp == 0 && np <= 8) {
+    // a few pieces: every thread loads its pieces' m, l and o at once and
+    // forms the weights itself (one round trip, no LDS)
+    uint16_t* out = (uint16_t*)a.out;
+    for (int idx = tid; idx < g * D; idx += 256) {
+      const int c = idx / D;
+      const int dd = idx - c * D;
+      const int64_t row = (int64_t)s * hq + h * g + c;
+      float mv[8], lv[8], ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jj = min(j, np - 1);
+        mv[j] = a.part_m[row * P + jj];
+        lv[j] = a.part_l[row * P + jj];
+        ov[j] = a.part_o[(row * P + jj) * D + dd];
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < np) M = fmaxf(M, mv[j]);
+      float wsum = 0.f, acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < np) {
+          const float wt = lv[j] * expf(mv[j] - M);
+          wsum += wt;
+          acc = fmaf(wt, ov[j], acc);
+        }
+      out[row * D + dd] = f32_to_bf16(acc / wsum);
+    }
+    return;
+  }
   for (int idx = tid; idx < g * n; idx += 256) {
     const int c = idx / n;
     const int j = idx - c * n;
@@ -916,34 +837,29 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     // 200 for 8 waves x 4 per CU, 191 for 4 waves x 4, 194 for 1 wave x 16).
     constexpr int NW = 8, NWS = 2;
     const int nw = a.seq_prefix ? NWS : NW;
-    // wave-merge area [nw][g][D] + [nw][16] x 3 (reference, l, maximum), also used for
-    // the piece weights of a merge ([2][g][P] + [g])
-    // (the shared-prefix variant merges in a separate kernel)
+    // wave-merge area [nw][g][D] + [nw][16] x 3 (reference, l, maximum),
+    // aliased with the per-wave granule slots (K + V of 16 tokens)
     const size_t wave_area = (size_t)nw * g * D + 3 * nw * 16;
-    const size_t merge_area = (size_t)2 * g * a.max_partitions + g;
-    const size_t words = a.seq_prefix ? wave_area : max(wave_area, merge_area);
-    // per-wave granule slots (K + V of 16 tokens), aliased with the merge areas
-    const size_t lds = max(words * sizeof(float), (size_t)nw * 64 * D);
-    if (lds > kDecodeLdsMax) return -2;
+    const size_t lds = max(wave_area * sizeof(float), (size_t)nw * 64 * D);
+    // the fold's general path stages [2][g][pieces + prefix partials] + [g] weights
+    const size_t flds = (size_t)(2 * g * (a.max_partitions + a.num_splits) + g) * sizeof(float);
+    if (lds > kDecodeLdsMax || flds > kDecodeLdsMax) return -2;
     // (the shared-prefix entry runs only with 16-token blocks)
     auto kern = a.seq_prefix ? decode_bf16_kernel<D, NWS, true, 16>
                 : a.bs_shift ? decode_bf16_kernel<D, NW, false, 32>
                              : decode_bf16_kernel<D, NW, false, 16>;
     const int variant = a.seq_prefix ? 1 : a.bs_shift ? 2 : 0;
     static std::atomic<uint64_t> attr_set[3];   // per variant, one bit per device
-    if (raise_lds_limit((const void*)kern, &attr_set[variant])) return -4;
+    static std::atomic<uint64_t> fold_attr;
+    if (raise_lds_limit((const void*)kern, &attr_set[variant]) ||
+        raise_lds_limit((const void*)decode_fold_kernel<D>, &fold_attr))
+      return -4;
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     // (tagged words, nothing to clear)
     kern<<<a.seq_prefix ? 4 * a.num_workgroups : a.num_workgroups, nw * kWave, lds, st>>>(a);
-    if (a.seq_prefix) {
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return -4;
-      const size_t flds = (size_t)(2 * g * (a.max_partitions + a.num_splits) + g) * sizeof(float);
-      if (flds > kDecodeLdsMax) return -2;
-      static std::atomic<uint64_t> fold_attr;
-      if (raise_lds_limit((const void*)decode_fold_kernel<D>, &fold_attr)) return -4;
-      decode_fold_kernel<D><<<(unsigned)units, 256, flds, st>>>(a);
-    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return -4;
+    decode_fold_kernel<D><<<(unsigned)units, 256, flds, st>>>(a);
     return status_of(hipGetLastError());
   }
   const int n_part = a.max_partitions - 1;   // fixed partitions of the fp32 path
@@ -976,7 +892,7 @@ int decode_scratch(hipStream_t st, uint8_t** base) {
   if (!addr[dev]) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -4;
-    // arrival words start at zero (no call's tag is zero); the partials need
+    // piece-count words start at zero (no call's tag is zero); the partials need
     // no initial value
     constexpr int64_t words = (int64_t)(kScratchArriveBytes / 8);
     zero_words_kernel<<<(unsigned)(words / 256 / 8), 256, 0, st>>>((uint64_t*)p, words);

@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_workspace_size_formula(lib):
     """pieces P = ceil(max_context_len / piece) + 1 per (sequence, query
-    head), each (o[D], m, l) in fp32, then one uint64 arrival word per
+    head), each (o[D], m, l) in fp32, then one uint64 piece-count word per
     (sequence, KV head); the piece is 512 tokens unless given."""
     ws = lib.paged_attention_decode_workspace_size
     assert ws(64, 32, 8, 128, 4096, 512) == 64 * 32 * 9 * 130 * 4 + 64 * 8 * 8
@@ -128,7 +128,7 @@ def test_empty_calls_are_no_ops(lib):
 
 
 def test_shared_workspace_layout(lib):
-    """The plain decode's regions (pieces, then one 64-bit arrival word per
+    """The plain decode's regions (pieces, then one 64-bit piece-count word per
     (sequence, KV head)), then seq_prefix [S] 64-bit words, then at the
     next 256-byte boundary the prefix partials o [S][Hq][NS][D], m, l.  NS:
     the prefix pass aims at one workgroup per compute unit (256 on MI355X,

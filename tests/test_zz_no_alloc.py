@@ -34,7 +34,7 @@ def _both(case, ptok):
 def test_noalloc_matches_workspace_entry_twice(gpu):
     tol = {"bf16": 2e-2, "fp32": 1e-5}
     # a larger call, then a smaller one: the second reuses the array the
-    # first left behind (other offsets, stale pieces and arrival words)
+    # first left behind (other offsets, stale pieces and piece-count words)
     for case, ptok in [(decode_case(951, 24, 1, 3000, 32, 8, 128, "bf16"), 0),
                        (decode_case(952, 5, 1, 700, 32, 8, 128, "bf16"), 64),
                        (decode_case(953, 3, 1, 300, 8, 2, 64, "fp32"), 32)]:
