@@ -842,7 +842,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": ("paged_attention_decode_shared (prefix pass extend_bf16_kernel<PREFIX> "
                            "+ decode_bf16_kernel<SHARED> + decode_fold_kernel)" if r.get("shared")
-                           else "paged_attention_decode (decode_bf16_kernel, merge fused)"),
+                           else "paged_attention_decode (decode_bf16_kernel + decode_fold_kernel)"),
                 **timing, "bytes_per_launch": int(per_launch)}
         if not args.no_ceiling:
             ceil = bandwidth_ceilings(torch, lib)
