@@ -304,10 +304,10 @@ size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t nu
  *                  bytes, 8-byte aligned: the paged_attention_decode layout
  *                  (o, m, l pieces, then one 64-bit word per (sequence, KV
  *                  head) holding the unit's piece count), then seq_prefix
- *                  [num_seqs] 64-bit words (the block each sequence's own
- *                  pass starts at, in bits 0..19, and how many prefix
- *                  partials it folds in, in bits 20..23), then at the next
- *                  256-byte boundary the prefix partials o
+ *                  [num_seqs] 64-bit words (where each sequence's own pass
+ *                  starts, in 16-token granules, in bits 0..19, and how
+ *                  many prefix partials it folds in, in bits 20..23), then
+ *                  at the next 256-byte boundary the prefix partials o
  *                  [num_seqs][num_q_heads][NS][head_dim], m and l
  *                  [num_seqs][num_q_heads][NS] fp32 (NS key splits).  Every
  *                  64-bit word carries the writing call's tag in bits 24..63,
@@ -321,12 +321,13 @@ size_t paged_attention_decode_shared_workspace_size(int32_t num_seqs, int32_t nu
  * min(prefix_blocks, (context_len - 1) / block_size) table entries must be
  * the first member's (the call reads the prefix blocks from the first
  * member's row only), and the first member must hold all prefix_blocks.
- * Otherwise the result is undefined, but every access stays inside the pool.  fp32 inputs,
- * block_size 32, or no groups, run paged_attention_decode unchanged.  Errors as
- * paged_attention_decode; PKV_ERR_UNSUPPORTED when the merge weights,
- * 2 x group x (P + NS) + group fp32 words, exceed the LDS; PKV_ERR_INVALID
- * when the prefix splits cover 2^20 blocks or more (the start block would
- * not fit its 20 bits).
+ * Otherwise the result is undefined, but every access stays inside the
+ * pool.  Block sizes 16 and 32 (group_prefix_blocks counts table entries of
+ * block_size tokens); fp32 inputs, or no groups, run paged_attention_decode
+ * unchanged.  Errors as paged_attention_decode; PKV_ERR_UNSUPPORTED when the
+ * merge weights, 2 x group x (P + NS) + group fp32 words, exceed the LDS;
+ * PKV_ERR_INVALID when the prefix splits cover 2^20 granules of 16 tokens or
+ * more (the start would not fit its 20 bits).
  */
 int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
                                   const void* v_pool, int32_t num_blocks,

@@ -500,9 +500,8 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   if (num_groups < 0 || max_group_size < 0 || max_prefix_blocks < 0)
     return fail(PKV_ERR_INVALID, "negative group argument");
   if (dtype != PKV_DTYPE_BF16 || num_groups == 0 || max_group_size == 0 ||
-      max_prefix_blocks == 0 || block_size != 16)
-    // nothing shared (or fp32, or 32-token blocks, which have no prefix
-    // pass): the plain decode
+      max_prefix_blocks == 0)
+    // nothing shared (or fp32, which has no prefix pass): the plain decode
     return paged_attention_decode(out, q, k_pool, v_pool, num_blocks, block_tables,
                                   max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                                   num_q_heads, num_kv_heads, head_dim, block_size, scale,
@@ -530,8 +529,8 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
     return fail(PKV_ERR_UNSUPPORTED,
                 "max_context_len %d over partition_size %d gives %lld pieces per context; use a "
                 "larger partition_size", max_context_len, ptok, (long long)P);
-  // a sequence's start block travels in 20 bits of its tagged word
-  if ((int64_t)sp.count * sp.blocks >= (1 << 20))
+  // a sequence's start (in 16-token granules) travels in 20 bits of its tagged word
+  if ((int64_t)sp.count * sp.blocks * (block_size / 16) >= (1 << 20))
     return fail(PKV_ERR_INVALID, "max_prefix_blocks %d too large", max_prefix_blocks);
   rc = check_positions(num_seqs, num_kv_heads, max_blocks_per_seq, P, ptok, block_size);
   if (rc) return rc;
@@ -564,7 +563,8 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
-  a.partition_blocks = ptok / block_size;
+  a.partition_blocks = ptok / 16;   // in 16-token granules
+  a.bs_shift = block_size == 32 ? 1 : 0;
   a.max_partitions = (int32_t)P;
   a.num_workgroups = decode_workgroups();
   a.scale = scale;
@@ -596,6 +596,7 @@ int paged_attention_decode_shared(void* out, const void* q, const void* k_pool,
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.head_dim = head_dim;
+  p.block_size = block_size;
   p.split_blocks = sp.blocks;
   p.num_splits = sp.count;
   p.scale = scale;

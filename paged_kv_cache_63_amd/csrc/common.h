@@ -177,7 +177,8 @@ struct PrefixArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t split_blocks;      // a multiple of 4
+  int32_t block_size;        // tokens per table entry (16 or 32)
+  int32_t split_blocks;      // table entries per key split, a multiple of 4
   int32_t num_splits;
   float scale;
 };

@@ -214,10 +214,10 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   const int W = gridDim.x;
   const int w = blockIdx.x;
   uint16_t* out = (uint16_t*)a.out;
-  // Shared-prefix decode: sequence s's own pass covers its blocks from
-  // start_block(s) on (the prefix pass covers those before); the start
-  // block sits in the sequence's word, which counts only if the prefix pass
-  // of this call wrote it.
+  // Shared-prefix decode: sequence s's own pass covers its 16-token
+  // granules from start_block(s) on (the prefix pass covers those before);
+  // the start sits in the sequence's word, which counts only if the prefix
+  // pass of this call wrote it.
   auto start_block = [&](int s, int nb) {
     if constexpr (SHARED) {
       const uint64_t v = a.seq_prefix[s];
@@ -476,7 +476,12 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < g * D; idx += NT) {
+    // (with 32-token blocks the thread id is taken opaque here, so that the
+    // compiler does not keep this loop's addresses live across the piece
+    // loop: they would not fit the register budget)
+    int tid_m = tid;
+    if constexpr (BS == 32) asm volatile("" : "+v"(tid_m));
+    for (int idx = tid_m; idx < g * D; idx += NT) {
       const int c = idx / D;
       const int dd = idx - c * D;
       // the piece's maximum; each wave's o and l are relative to its own
@@ -844,12 +849,12 @@ int launch_d(const DecodeArgs& a, int32_t dtype, hipStream_t st) {
     // the fold's general path stages [2][g][pieces + prefix partials] + [g] weights
     const size_t flds = (size_t)(2 * g * (a.max_partitions + a.num_splits) + g) * sizeof(float);
     if (lds > kDecodeLdsMax || flds > kDecodeLdsMax) return -2;
-    // (the shared-prefix entry runs only with 16-token blocks)
-    auto kern = a.seq_prefix ? decode_bf16_kernel<D, NWS, true, 16>
+    auto kern = a.seq_prefix ? (a.bs_shift ? decode_bf16_kernel<D, NWS, true, 32>
+                                           : decode_bf16_kernel<D, NWS, true, 16>)
                 : a.bs_shift ? decode_bf16_kernel<D, NW, false, 32>
                              : decode_bf16_kernel<D, NW, false, 16>;
-    const int variant = a.seq_prefix ? 1 : a.bs_shift ? 2 : 0;
-    static std::atomic<uint64_t> attr_set[3];   // per variant, one bit per device
+    const int variant = (a.seq_prefix ? 2 : 0) + (a.bs_shift ? 1 : 0);
+    static std::atomic<uint64_t> attr_set[4];   // per variant, one bit per device
     static std::atomic<uint64_t> fold_attr;
     if (raise_lds_limit((const void*)kern, &attr_set[variant]) ||
         raise_lds_limit((const void*)decode_fold_kernel<D>, &fold_attr))

@@ -219,17 +219,18 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     if (row0 == 0 && h == 0 && split == 0) {
       // each member's own pass starts at its first block past the prefix
       // that still leaves it one token (the decoded one): its last block
+      // (the word holds that start in 16-token granules, the decode's unit)
       for (int m = threadIdx.x; m < n; m += NW * kWave) {
         const int s = a.group_seqs[goff + m];
         if (s < 0 || s >= a.num_seqs) continue;
         const int Ls = a.context_lens[s];
-        const uint64_t start = Ls >= 1 ? min(pblk, (Ls - 1) / kBs) : 0;
+        const uint64_t start = Ls >= 1 ? min(pblk, (Ls - 1) / BS) : 0;
         const uint64_t nsp = Ls >= 1 ? (pblk + a.split_blocks - 1) / a.split_blocks : 0;
-        a.seq_prefix[s] = a.tag | (nsp << 20) | start;
+        a.seq_prefix[s] = a.tag | (nsp << 20) | (start * SPB);
       }
     }
-    const int klo = split * a.split_blocks * kBs;
-    L = min(pblk * kBs, klo + a.split_blocks * kBs);   // keys at or past L are masked
+    const int klo = split * a.split_blocks * BS;
+    L = min(pblk * BS, klo + a.split_blocks * BS);   // keys at or past L are masked
     if (klo >= L) return;
     kt0 = klo / KT;
     r = a.group_seqs[goff];     // the first member's table supplies the prefix blocks
@@ -276,8 +277,8 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     const bool live = s >= 0 && s < a.num_seqs;
     const int j = rr - (rr / g) * g;
     const int Ls = live ? a.context_lens[s] : 0;
-    const int start = Ls >= 1 ? min(pblk, (Ls - 1) / kBs) : 0;
-    qpos = live ? min(start * kBs, L) - 1 : -1;
+    const int start = Ls >= 1 ? min(pblk, (Ls - 1) / BS) : 0;
+    qpos = live ? min(start * BS, L) - 1 : -1;
     qrow = qp + ((int64_t)(live ? s : 0) * hq + h * g + (live ? j : 0)) * D + G * 8;
     qlive = live;
     int lo = live ? qpos : (1 << 30), hi = live ? qpos : -1;
@@ -821,8 +822,12 @@ int launch_p(const PrefixArgs& a, hipStream_t st) {
   const int64_t grid = (int64_t)kXcds * unit_groups * tiles;
   if (grid == 0) return 0;
   if (grid > 0x7fffffff || units > 0x7fffffff) return -1;
-  extend_bf16_kernel<D, true, PrefixArgs, 16><<<(unsigned)grid, 8 * kWave, 0, st>>>(a, tiles,
-                                                                                   (int)units);
+  if (a.block_size == 32)
+    extend_bf16_kernel<D, true, PrefixArgs, 32><<<(unsigned)grid, 8 * kWave, 0, st>>>(a, tiles,
+                                                                                     (int)units);
+  else
+    extend_bf16_kernel<D, true, PrefixArgs, 16><<<(unsigned)grid, 8 * kWave, 0, st>>>(a, tiles,
+                                                                                     (int)units);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

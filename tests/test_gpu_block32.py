@@ -137,13 +137,14 @@ def test_extend_at_block_size_32(gpu, dtype, R, plo, phi, nlo, nhi, hq, hkv, d):
     assert err <= TOL[dtype], err
 
 
-def test_shared_entry_at_block_size_32_is_the_plain_decode(gpu):
-    """32-token blocks have no prefix pass: the shared-prefix entry runs the
-    plain decode, and returns its result."""
+def test_shared_entry_at_block_size_32_without_groups_is_the_plain_decode(gpu):
+    """With no groups the shared-prefix entry at 32-token blocks runs the
+    plain decode and returns its bits (the forked families at 32-token
+    blocks, with a prefix pass, are in the shared-prefix tests)."""
     case = decode_case(3601, 6, 100, 600, 32, 8, 128, "bf16", block_size=32)
     st = Decode32(case, 32)
-    groups = _lib.groups_to_device((np.array([0, 6], np.int32), np.arange(6, dtype=np.int32),
-                                    np.array([2], np.int32), 6, 2))
+    groups = _lib.groups_to_device((np.array([0], np.int32), np.zeros(0, np.int32),
+                                    np.zeros(0, np.int32), 0, 0))
     out = torch.empty_like(st.q)
     _lib.paged_attention_decode_shared(out, st.q, st.k, st.v, st.tables, st.lens,
                                        int(max(case.context_lens)), case.scale, groups)

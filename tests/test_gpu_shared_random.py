@@ -2,8 +2,8 @@
 the oracle's plain decode.  Each case draws its own batch: one to four
 parents with prompts of various lengths, each forked into up to six children
 (some early, before the parent grows on), children with empty to long
-suffixes, lone sequences, a GQA ratio from 1 to 16, head dim 64 or 128 and a
-partition size.  The block manager runs the same operations on both sides
+suffixes, lone sequences, a GQA ratio from 1 to 16, head dim 64 or 128, a
+partition size, and blocks of 16 tokens (of 32 in the last cases).  The block manager runs the same operations on both sides
 (forks share blocks, a write into a shared partial block copies it first),
 the groups come from the host helper, and the result must equal attention
 over each sequence's own tokens (Triptych page, technical summary: sharing
@@ -21,7 +21,7 @@ from workloads import normal_words
 pytestmark = pytest.mark.gpu
 
 HEADS = [(8, 2), (32, 8), (16, 1), (4, 4), (64, 8), (12, 4)]
-NB = 4096
+TOKENS = 4096 * 16   # pool capacity in tokens
 
 
 def _script(rng):
@@ -41,17 +41,18 @@ def _script(rng):
     return ops
 
 
-def _run(side, ops, order, seed, hq, hkv, d):
+def _run(side, ops, order, seed, hq, hkv, d, bs):
     """Run ``ops`` on one side ('lib' or 'oracle'), K/V of every appended
     token drawn in op order from one seeded generator, then one decode step
     for every sequence."""
     rng = np.random.default_rng(seed)
+    nb = TOKENS // bs
     if side == "lib":
-        bm = BlockAllocator(NB, 16, max_seqs=64, max_blocks_per_seq=128, free_order=order)
-        k, v = poisoned_pools(NB, hkv, d, "bf16")
+        bm = BlockAllocator(nb, bs, max_seqs=64, max_blocks_per_seq=2048 // bs, free_order=order)
+        k, v = poisoned_pools(nb, hkv, d, "bf16", bs=bs)
     else:
-        bm = block_manager.RefBlockManager(NB, 16, order)
-        k, v = paging.new_pools(NB, hkv, d, 16, "bf16")
+        bm = block_manager.RefBlockManager(nb, bs, order)
+        k, v = paging.new_pools(nb, hkv, d, bs, "bf16")
     ids = {}
 
     def write(slots, pairs, kw, vw):
@@ -61,7 +62,7 @@ def _run(side, ops, order, seed, hq, hkv, d):
             _lib.paged_kv_append(to_dev(kw, "bf16"), to_dev(vw, "bf16"), i32(slots), k, v)
         else:
             paging.copy_blocks(k, v, np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
-            paging.append(k, v, kw, vw, np.asarray(slots), 16)
+            paging.append(k, v, kw, vw, np.asarray(slots), bs)
 
     for op in ops:
         if op[0] == "new":
@@ -102,20 +103,20 @@ def _run(side, ops, order, seed, hq, hkv, d):
     return dict(k=k, v=v, tables=tables, lens=lens, q=q)
 
 
-@pytest.mark.parametrize("seed", range(16))
-def test_shared_decode_random_family(gpu, seed):
+@pytest.mark.parametrize("seed,bs", [(s, 16) for s in range(16)] + [(s, 32) for s in range(16, 24)])
+def test_shared_decode_random_family(gpu, seed, bs):
     rng = np.random.default_rng(9300 + seed)
     hq, hkv = HEADS[int(rng.integers(len(HEADS)))]
     d = int(rng.choice([64, 128]))
-    ptok = int(rng.choice([0, 16, 64, 256]))
+    ptok = int(rng.choice([0, bs, 64, 256]))
     ops = _script(rng)
-    order = rng.permutation(NB)
-    lib = _run("lib", ops, order, 9300 + seed, hq, hkv, d)
-    ref = _run("oracle", ops, order, 9300 + seed, hq, hkv, d)
+    order = rng.permutation(TOKENS // bs)
+    lib = _run("lib", ops, order, 9300 + seed, hq, hkv, d, bs)
+    ref = _run("oracle", ops, order, 9300 + seed, hq, hkv, d, bs)
     w = ref["tables"].shape[1]
     assert np.array_equal(lib["tables"][:, :w], ref["tables"])
     assert np.array_equal(lib["lens"], ref["lens"])
-    groups = shared_prefix_groups(lib["tables"], lib["lens"])
+    groups = shared_prefix_groups(lib["tables"], lib["lens"], block_size=bs)
     scale = float(np.float32(1.0 / np.sqrt(d)))
     q = to_dev(lib["q"], "bf16")
     out = torch.full_like(q, float("nan"))
@@ -123,10 +124,53 @@ def test_shared_decode_random_family(gpu, seed):
                                        i32(lib["lens"]), int(lib["lens"].max()), scale,
                                        _lib.groups_to_device(groups), ptok)
     want = attention.decode(ref["q"], ref["k"], ref["v"], ref["tables"], ref["lens"],
-                            np.float32(scale), 16, "bf16")
+                            np.float32(scale), bs, "bf16")
     got = f64_of(out)
     err = np.abs(got - want).max()
     print(f"seqs={len(ref['lens'])} groups={len(groups[2])} max_group={groups[3]} "
           f"max_prefix_blocks={groups[4]} max_len={int(ref['lens'].max())} hq={hq} hkv={hkv} "
-          f"d={d} ptok={ptok}: max |err| {err:.3e}")
+          f"d={d} ptok={ptok} bs={bs}: max |err| {err:.3e}")
     assert np.isfinite(got).all() and err <= 2e-2, err
+
+
+def test_shared_decode_block_32_family(gpu):
+    """A hand-made family at 32-token blocks: a 300-token prompt (nine full
+    blocks and a partly filled one) forked into samples that decode at once
+    (the shared partial block is copied on the first write), fill it to the
+    boundary, or grow past it; a prompt shorter than one block forked too (no
+    full block to share: no group); a lone sequence of exactly two blocks.
+    The prompt family must form one group over the nine full blocks, and
+    every output must be the oracle's plain decode within the bf16
+    tolerance."""
+    bs, hq, hkv, d = 32, 32, 8, 128
+    ops = [("new", "P"), ("add", "P", 300),
+           ("fork", "P", "A"),
+           ("fork", "P", "B"), ("add", "B", 20),
+           ("fork", "P", "C"), ("add", "C", 100),
+           ("add", "P", 4),
+           ("new", "Q"), ("add", "Q", 31), ("fork", "Q", "Q1"),
+           ("new", "L"), ("add", "L", 64)]
+    order = np.random.default_rng(9400).permutation(TOKENS // bs)
+    lib = _run("lib", ops, order, 9401, hq, hkv, d, bs)
+    ref = _run("oracle", ops, order, 9401, hq, hkv, d, bs)
+    w = ref["tables"].shape[1]
+    assert np.array_equal(lib["tables"][:, :w], ref["tables"])
+    offs, seqs, pblk, max_size, max_pb = shared_prefix_groups(lib["tables"], lib["lens"],
+                                                              block_size=bs)
+    # names sort as A B C L P Q Q1: the prompt family is rows 0, 1, 2 and 4
+    assert len(pblk) == 1 and int(pblk[0]) == 9
+    assert sorted(seqs[offs[0]:offs[1]].tolist()) == [0, 1, 2, 4]
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    q = to_dev(lib["q"], "bf16")
+    want = attention.decode(ref["q"], ref["k"], ref["v"], ref["tables"], ref["lens"],
+                            np.float32(scale), bs, "bf16")
+    for ptok in (0, 64):
+        out = torch.full_like(q, float("nan"))
+        _lib.paged_attention_decode_shared(out, q, lib["k"], lib["v"], i32(lib["tables"]),
+                                           i32(lib["lens"]), int(lib["lens"].max()), scale,
+                                           _lib.groups_to_device((offs, seqs, pblk, max_size,
+                                                                  max_pb)), ptok)
+        got = f64_of(out)
+        err = np.abs(got - want).max()
+        print(f"block 32 family, partition {ptok}: max |err| {err:.3e}")
+        assert np.isfinite(got).all() and err <= 2e-2, err
