@@ -35,14 +35,16 @@
  * Pool layout (both pools hold num_blocks blocks; e = element):
  *    k_pool  [num_blocks][num_kv_heads][block_size][head_dim]
  *            -- a key vector is one contiguous row.
- *    v_pool  [num_blocks][num_kv_heads][head_dim][block_size]
- *            -- values are stored transposed inside a block: one row of
- *               block_size tokens per channel, in which the token at
- *               offset `off` sits at position v_pos(off) = off with bits
- *               2 and 3 exchanged (order 0-3, 8-11, 4-7, 12-15, then the
- *               same for 16-31 in a 32-token block; the map is its own
- *               inverse).  This is the order in which the matrix cores
- *               consume a block's tokens, two 8-byte halves per lane.
+ *    v_pool  [num_blocks][num_kv_heads] slabs of head_dim x block_size
+ *            elements -- values are stored transposed, in 16-token halves
+ *            [block_size / 16][head_dim][16]: one row of 16 tokens per
+ *            channel in each half (a 32-token block is two halves, one
+ *            after the other), and in a row the token at offset `off` of
+ *            its half sits at position v_pos(off) = off with bits 2 and 3
+ *            exchanged (order 0-3, 8-11, 4-7, 12-15; the map is its own
+ *            inverse).  This is the order in which the matrix cores consume
+ *            a block's tokens, two 8-byte halves per lane, and the values
+ *            of any 16 consecutive tokens of a block are contiguous.
  *  A slot is phys_block * block_size + offset_in_block.
  *
  * Safety: kernels never touch memory outside the ranges the arguments
@@ -123,7 +125,7 @@ int copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks,
  *
  *   dst_k, dst_v   pools of dst_num_blocks blocks in the layout above (K
  *                  [..][num_kv_heads][block_size][head_dim], V
- *                  [..][num_kv_heads][head_dim][block_size]), written
+ *                  [..][num_kv_heads] slabs of head_dim x block_size), written
  *   src_k, src_v   pools of src_num_blocks blocks, same layout, read
  *   block_mapping  [num_pairs][2] int32, device memory: (src block, dst block)
  *

@@ -13,11 +13,15 @@ oracle reproduces, element for element):
 
   * K pool: ``[num_blocks][num_kv_heads][B][head_dim]`` -- one token's key is a
     contiguous row of ``head_dim`` words.
-  * V pool: ``[num_blocks][num_kv_heads][head_dim][B]`` -- within a block the
-    value vectors are stored transposed, one row of B tokens per channel,
-    and inside a row the token at offset ``off`` sits at position
-    ``v_pos(off)``: bits 2 and 3 of the offset exchanged (for B = 16 the
-    order is tokens 0-3, 8-11, 4-7, 12-15; the map is its own inverse).
+  * V pool: ``[num_blocks][num_kv_heads]`` slabs of ``head_dim * B`` words.
+    A slab holds the block's value vectors transposed, in ``B / 16`` halves
+    of 16 tokens: half ``off // 16`` is ``[head_dim][16]``, one row of 16
+    tokens per channel, and inside a row the token at offset ``off % 16``
+    sits at position ``v_pos(off % 16)``: bits 2 and 3 of the offset
+    exchanged (tokens 0-3, 8-11, 4-7, 12-15; the map is its own inverse).
+    For B = 16 this is ``[head_dim][16]``; the array's shape is
+    ``[num_blocks][num_kv_heads][head_dim][B]`` for every B, a container
+    of the slab's words (:func:`v_halves` gives the view by halves).
 
 A *slot* names one token position in the pool: ``slot = phys_block * B + off``
 with ``off`` in ``[0, B)``.  Logical position ``pos`` of a sequence lives in
@@ -33,6 +37,16 @@ def v_pos(off):
     """Position of a block's token ``off`` inside a V channel row (bits 2
     and 3 exchanged).  Works on ints and integer arrays."""
     return (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1)
+
+
+def v_halves(v_pool):
+    """The V pool viewed by 16-token halves: ``[num_blocks][num_kv_heads]
+    [B / 16][head_dim][16]``, the same words (token ``off`` of a block, channel
+    ``c``: ``[blk, h, off // 16, c, v_pos(off % 16)]``).  A block of fewer
+    than 16 tokens (the model's small test blocks) is one ``[head_dim][B]``
+    part."""
+    nb, hkv, d, bs = v_pool.shape
+    return v_pool.reshape(nb, hkv, max(bs // 16, 1), d, min(bs, 16))
 
 
 def slot_of(table_row, pos: int, block_size: int) -> int:
@@ -67,13 +81,14 @@ def append(k_pool, v_pool, k_new, v_new, slot_mapping, block_size: int) -> None:
     caller guarantees it), so the order of the writes does not matter.
     """
     slots = np.asarray(slot_mapping, dtype=np.int64)
+    vh = v_halves(v_pool)
     for t in range(slots.shape[0]):
         s = int(slots[t])
         if s < 0:
             continue
         blk, off = s // block_size, s % block_size
         k_pool[blk, :, off, :] = k_new[t]
-        v_pool[blk, :, :, v_pos(off)] = v_new[t]
+        vh[blk, :, off // 16, :, v_pos(off % 16)] = v_new[t]
 
 
 def copy_blocks(k_pool, v_pool, block_mapping) -> None:
@@ -117,11 +132,12 @@ def gather(k_pool, v_pool, table_row, context_len: int, block_size: int):
     _, hkv, _, d = k_pool.shape
     k_out = np.empty((context_len, hkv, d), dtype=k_pool.dtype)
     v_out = np.empty((context_len, hkv, d), dtype=v_pool.dtype)
+    vh = v_halves(v_pool)
     for pos in range(context_len):
         blk = int(table_row[pos // block_size])
         off = pos % block_size
         k_out[pos] = k_pool[blk, :, off, :]
-        v_out[pos] = v_pool[blk, :, :, v_pos(off)]
+        v_out[pos] = vh[blk, :, off // 16, :, v_pos(off % 16)]
     return k_out, v_out
 
 
@@ -134,10 +150,10 @@ def gather_fast(k_pool, v_pool, table_row, context_len: int, block_size: int):
     nblk = -(-context_len // block_size)
     ids = np.asarray(table_row[:nblk], dtype=np.int64)
     kb = k_pool[ids]                               # [nblk][Hkv][B][D]
-    vb = v_pool[ids][..., v_pos(np.arange(block_size))]   # [nblk][Hkv][D][B], token order
+    vb = v_halves(v_pool)[ids][..., v_pos(np.arange(16))]   # [nblk][Hkv][B/16][D][16], token order
     _, hkv, _, d = k_pool.shape
     k_out = kb.transpose(0, 2, 1, 3).reshape(nblk * block_size, hkv, d)[:context_len]
-    v_out = vb.transpose(0, 3, 1, 2).reshape(nblk * block_size, hkv, d)[:context_len]
+    v_out = vb.transpose(0, 2, 4, 1, 3).reshape(nblk * block_size, hkv, d)[:context_len]
     return np.ascontiguousarray(k_out), np.ascontiguousarray(v_out)
 
 

@@ -125,7 +125,8 @@ def _pools(k_pool, v_pool, host_ok=False):
         raise ValueError("pools must be 4-D")
     nb, hkv, bs, d = k_pool.shape
     if tuple(v_pool.shape) != (nb, hkv, d, bs):
-        raise ValueError(f"v_pool must be [num_blocks][Hkv][D][B] = {(nb, hkv, d, bs)}, "
+        raise ValueError(f"v_pool must be [num_blocks][Hkv][D][B] (one D x B slab per block "
+                         f"and head, stored in 16-token halves) = {(nb, hkv, d, bs)}, "
                          f"got {tuple(v_pool.shape)}")
     if k_pool.dtype != v_pool.dtype or k_pool.dtype not in PKV_DTYPE:
         raise ValueError("pools must share a dtype in (float32, bfloat16)")

@@ -22,12 +22,21 @@ __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t w) { return __uint_as_float((uint32_t)w << 16); }
 
-// Position of in-block token offset `off` inside a V channel row: bits 2 and
-// 3 exchanged, so a row holds tokens 0-3, 8-11, 4-7, 12-15.  A matrix-core
-// operand that needs tokens {4G..4G+3, 8+4G..8+4G+3} then reads 16
-// contiguous bytes.  The map is its own inverse.
+// Position of a token's offset `off` (0..15) inside a 16-token V channel
+// row: bits 2 and 3 exchanged, so a row holds tokens 0-3, 8-11, 4-7, 12-15.
+// A matrix-core operand that needs tokens {4G..4G+3, 8+4G..8+4G+3} then
+// reads 16 contiguous bytes.  The map is its own inverse.
 __host__ __device__ __forceinline__ int v_pos(int off) {
   return (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1);
+}
+
+// V slab of one (block, head): the block's values transposed, in 16-token
+// halves ([B/16][D][16]: a 32-token block is two of them, so the values of
+// any 16-token granule are one contiguous run of 16 x D elements).  Element
+// offset of (in-block token off, channel c); channel rows are kVRow apart.
+constexpr int kVRow = 16;
+__host__ __device__ __forceinline__ int64_t v_elem(int off, int c, int d) {
+  return (int64_t)(off & ~15) * d + (int64_t)c * kVRow + v_pos(off & 15);
 }
 
 // fp32 -> bf16 word, round to nearest even (the gfx950 conversion instruction)

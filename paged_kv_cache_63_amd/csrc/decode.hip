@@ -69,7 +69,7 @@ __device__ __forceinline__ const uint8_t* uni(const uint8_t* p) {
 
 // Direct-to-LDS copies of one 16-token granule of one head into this wave's
 // LDS slot: dma_k moves the K rows (16 x D bf16, 32*D bytes at kbase),
-// dma_v the V half-rows (D channel rows of 16 tokens, 32 bytes each at
+// dma_v the V rows (D channel rows of 16 tokens, 32 bytes each at
 // vbase + row * vrow_bytes).  Every instruction moves 1 KB: lane l writes
 // slot bytes i*1024 + 16*l and reads the global chunk that belongs there
 // (koff, voff per lane; the K chunk positions are XOR-swizzled by row, so
@@ -276,13 +276,13 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
   // The kernel walks 16-token granules; a table entry covers 1 << sh of
   // them (block_size 16 << sh).  Granule b is part b & (2^sh - 1) of the
   // entry b >> sh: its keys are that part's 16 rows of the (block, head) K
-  // slab, its values the same 16 positions of each channel row of the V
-  // slab (channel rows of 16 << sh tokens).
+  // slab, its values that part's 16-token half of the V slab ([D][16]):
+  // both one contiguous run of 16 x D elements.
   constexpr int sh = BS == 32 ? 1 : 0;
   static_assert(BS == 16 || BS == 32, "block sizes 16 and 32");
   const int64_t head_elems = (int64_t)kBs * D;           // one granule of one head
   const int64_t slab_elems = head_elems << sh;           // one (block, head) slab
-  const int vrow = kBs << sh;                            // V channel row, elements
+  const int vrow = kVRow;                                // V channel row, elements
   const float sl2 = a.scale * kLog2e;
   const int P = a.max_partitions;
   float* sm_o = smem;                  // [NW][g][D]
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void decode_bf16_kernel(DecodeArgs a
     auto vaddr = [&](int j, int phys) {
       const int b = bb + wave + j * NW;
       return (const uint8_t*)(vpool + ((int64_t)phys * hkv + h) * slab_elems +
-                              (b & ((1 << sh) - 1)) * kBs);
+                              (b & ((1 << sh) - 1)) * head_elems);
     };
     auto issue_k = [&](int j, int phys) { dma_k<D>(kaddr(j, phys), dma_koff(opaque_lane()), lds_k); };
     auto issue_v = [&](int j, int phys) {
@@ -591,13 +591,13 @@ __global__ __launch_bounds__(kWave) void decode_f32_kernel(DecodeArgs a) {
   // 16-token granules; a table entry covers 1 << sh of them (as in the bf16
   // kernel)
   const int sh = a.bs_shift;
-  const int vrow = kBs << sh;
+  const int vrow = kVRow;
   for (int b = b0; b < b1; ++b) {
     const int phys = clamp_block(trow[b >> sh], a.num_blocks);
     const int part = b & ((1 << sh) - 1);
     const int64_t base = ((int64_t)phys * hkv + h) * (kBs << sh) * D;
-    const float* kb = kpool + base + part * kBs * D;
-    const float* vb = vpool + base + part * kBs;
+    const float* kb = kpool + base + part * kBs * D;   // the granule's keys and values:
+    const float* vb = vpool + base + part * kBs * D;   // 16 x D elements each
     const int nvalid = min(kBs, L - b * kBs);
     for (int idx = lane; idx < kBs * g; idx += kWave) {
       const int t = idx & (kBs - 1);

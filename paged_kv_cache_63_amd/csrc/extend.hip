@@ -161,20 +161,19 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
   constexpr int SWZ = 16 / CPR;           // consecutive key rows sharing one swizzle value
   constexpr int SUBB = kBs * ROWB;        // bytes of one 16-key sub-block of one head
   constexpr int BLKB = BS * ROWB;         // bytes of one (block, head) slab
-  constexpr int VROWB = BS * 2;           // bytes of one V channel row of a slab
+  constexpr int VROWB = kVRow * 2;        // bytes of one V channel row (a 16-token half of a slab)
   constexpr int TILEB = NSB * SUBB;       // bytes of a K (or V) tile
   constexpr int SEGS = TILEB / 16 / kWave;  // 64-chunk segments per K (or V) tile
   constexpr int PER_T = 2 * SEGS / NW;    // direct-to-LDS loads per thread per tile
   constexpr int NST = 5;                  // LDS ring stages (160 KB for D = 128)
   static_assert(PER_T * NW == 2 * SEGS, "tile must split evenly over the waves");
   static_assert(BS == 16 || BS == 32, "block sizes 16 and 32");
-  // V rows in LDS: the 16-byte chunks of channel row c are permuted by an
-  // XOR with vswz(c), so that the 16 lanes of one read phase (channels
-  // c..c+15, the same chunk) hit 16 distinct 4-bank groups: 32-byte rows
-  // (BS 16) repeat the banks every 8 channels, 64-byte rows (BS 32) every 4.
-  auto vswz = [](int c) -> int {
-    return BS == 16 ? (((c >> 2) ^ (c >> 3)) & 1) : ((c >> 2) & 3);
-  };
+  // V rows in LDS: the two 16-byte chunks of channel row c are exchanged
+  // where vswz(c) is set, so that the 16 lanes of one read phase (channels
+  // c..c+15, the same chunk) hit 16 distinct 4-bank groups (32-byte rows
+  // repeat the banks every 8 channels).  A slab's 16-token halves lie one
+  // after the other, [D][16] each, in the pool and in LDS alike.
+  auto vswz = [](int c) -> int { return ((c >> 2) ^ (c >> 3)) & 1; };
   // Rescale the accumulators only when a row's maximum has grown by more
   // than this many powers of two since the reference used for its
   // exponentials (the exponentials stay below 2^kLazy in between).
@@ -354,11 +353,9 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
     for (int ks = 0; ks < KS; ++ks)
       koff[ks] = (uint32_t)((c32 >> 4) * SUBB + row * ROWB + (((ks * 2 + G) ^ f) * 16));
   }
-  // V: sub-block part p of a slab is chunks 2p, 2p+1 of each channel row
-  uint32_t voff[SPB];
-#pragma unroll
-  for (int p = 0; p < SPB; ++p)
-    voff[p] = (uint32_t)(TILEB + c32 * VROWB + (((2 * p + G) ^ vswz(c32)) * 16));
+  // V: channel row c32 of a 16-key sub-block, chunk G (sub-block b of the
+  // tile at b * SUBB)
+  const uint32_t voff = (uint32_t)(TILEB + c32 * VROWB + ((G ^ vswz(c32)) * 16));
 
   const float c2 = a.scale * kLog2e;   // scores -> base-2 exponent units
   float m_ref = -INFINITY;
@@ -386,8 +383,7 @@ __global__ __launch_bounds__(8 * kWave) void extend_bf16_kernel(Args a, int tile
   constexpr int NPRE = NPV / 2;  // V fragments read at the end of the vector phase
   auto vread = [&](int st, int i) {
     const int b = i / DT;   // sub-block
-    return *reinterpret_cast<const bf16x8*>(kv_s[st] + voff[b % SPB] + (b / SPB) * BLKB +
-                                            (i % DT) * 32 * VROWB);
+    return *reinterpret_cast<const bf16x8*>(kv_s[st] + voff + b * SUBB + (i % DT) * 32 * VROWB);
   };
   auto kread = [&](int st, int i) {
     return *reinterpret_cast<const bf16x8*>(kv_s[st] + koff[i / 2] + (i % 2) * 2 * SUBB);
@@ -743,8 +739,8 @@ __global__ __launch_bounds__(kWave) void extend_f32_kernel(ExtendArgs a) {
     phys = (phys >= 0 && phys < a.num_blocks) ? phys : 0;
     const int part = b % spb;
     const int64_t base = ((int64_t)phys * hkv + h) * bsz * D;
-    const float* kb = kpool + base + part * kBs * D;
-    const float* vb = vpool + base + part * kBs;
+    const float* kb = kpool + base + part * kBs * D;   // the granule's keys and values:
+    const float* vb = vpool + base + part * kBs * D;   // 16 x D elements each
     const int nvalid = min(kBs, ctx - b * kBs);
     for (int idx = lane; idx < kBs * g; idx += kWave) {
       const int t = idx & (kBs - 1);
@@ -768,7 +764,7 @@ __global__ __launch_bounds__(kWave) void extend_f32_kernel(ExtendArgs a) {
         const float pt = expf(sc_s[j][t] - m_new);
         psum += pt;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pt, vb[(lane + e * kWave) * bsz + v_pos(t)], acc[e]);
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pt, vb[(lane + e * kWave) * kVRow + v_pos(t)], acc[e]);
       }
       l_run[j] = l_run[j] * alpha + psum;
       m_run[j] = m_new;

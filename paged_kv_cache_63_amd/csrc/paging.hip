@@ -1,10 +1,11 @@
 // Pool writes and reads that move bits only: append (token -> slot),
 // copy-on-write block copy, and the gather of one sequence's blocks.
 //
-// Pool layout: K [num_blocks][Hkv][B][D], V [num_blocks][Hkv][D][B] with
-// the tokens of a V channel row in the order v_pos (bits 2 and 3 of the
-// in-block offset exchanged: 0-3, 8-11, 4-7, 12-15).  Every thread moves one
-// 16-byte piece of a key or value row; all offsets are 64-bit.
+// Pool layout: K [num_blocks][Hkv][B][D]; V [num_blocks][Hkv] slabs of
+// B/16 channel-major 16-token halves [D][16], the tokens of a channel row in
+// the order v_pos (bits 2 and 3 of the offset exchanged: 0-3, 8-11, 4-7,
+// 12-15), see v_elem.  Every thread moves one 16-byte piece of a key or
+// value row; all offsets are 64-bit.
 #include "common.h"
 
 namespace pkv {
@@ -40,18 +41,18 @@ __device__ __forceinline__ void append_pieces(
     const int64_t head_base = ((int64_t)blk * hkv + h) * bs * row_bytes;  // bytes
     *reinterpret_cast<u32x4*>(k_pool + head_base + (int64_t)off * row_bytes + piece * 16) = kv;
     const int32_t c0 = piece * kPer;  // first channel of the piece
-    uint8_t* vrow = v_pool + head_base + ((int64_t)c0 * bs + v_pos(off)) * E;
+    uint8_t* vrow = v_pool + head_base + v_elem(off, c0, d) * E;
     if constexpr (E == 2) {
       const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
         const uint16_t x = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-        *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * bs * E) = x;
+        *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * kVRow * E) = x;
       }
     } else {
       const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * bs * E) = w[e];
+      for (int e = 0; e < kPer; ++e) *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * kVRow * E) = w[e];
     }
   }
 }
@@ -244,14 +245,14 @@ __global__ __launch_bounds__(kThreads) void append_bulk_kernel(
     const int64_t head_base = ((int64_t)blk * hkv + h) * bs * row_bytes;
     *reinterpret_cast<u32x4*>(k_pool + head_base + (int64_t)off * row_bytes + piece * 16) = kv;
     const int32_t c0 = piece * kPer;
-    uint8_t* vrow = v_pool + head_base + ((int64_t)c0 * bs + v_pos(off)) * E;
+    uint8_t* vrow = v_pool + head_base + v_elem(off, c0, d) * E;
     const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       if constexpr (E == 2)
-        *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * bs * E) = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+        *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * kVRow * E) = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
       else
-        *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * bs * E) = w[e];
+        *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * kVRow * E) = w[e];
     }
   }
 }
@@ -371,18 +372,18 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     const int64_t dst = row * row_bytes + (int64_t)piece * 16;
     *reinterpret_cast<u32x4*>(k_out + dst) =
         *reinterpret_cast<const u32x4*>(k_pool + head_base + (int64_t)off * row_bytes + piece * 16);
-    const uint8_t* vrow = v_pool + head_base + ((int64_t)piece * kPer * bs + v_pos(off)) * E;
+    const uint8_t* vrow = v_pool + head_base + v_elem(off, piece * kPer, d) * E;
     uint32_t w[4];
     if constexpr (E == 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(vrow + (int64_t)(2 * e) * bs * E);
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(vrow + (int64_t)(2 * e + 1) * bs * E);
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(vrow + (int64_t)(2 * e) * kVRow * E);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(vrow + (int64_t)(2 * e + 1) * kVRow * E);
         w[e] = lo | (hi << 16);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint32_t*>(vrow + (int64_t)e * bs * E);
+      for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint32_t*>(vrow + (int64_t)e * kVRow * E);
     }
     *reinterpret_cast<u32x4*>(v_out + dst) = u32x4{w[0], w[1], w[2], w[3]};
   }

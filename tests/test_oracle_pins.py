@@ -53,6 +53,27 @@ def test_pool_layout_by_hand():
                                                        4, 5, 6, 7, 12, 13, 14, 15]
 
 
+def test_pool_layout_by_hand_block_32():
+    """With 32-token blocks V is kept in two 16-token halves, each [D][16]:
+    the token at offset 21 of block 1 (second half, offset 5 = 0b0101 in it,
+    position 0b1001), head 0, channel 2 lands at flat word
+    16 * D + 2 * 16 + 9 of the (block 1, head 0) V slab, so that the values
+    of each 16-token half of a block are one contiguous run of 16 * D words;
+    its key is row 21 of the K slab."""
+    B, hkv, D = 32, 2, 4
+    kp, vp = paging.new_pools(3, hkv, D, B, "fp32")
+    k_new = np.arange(hkv * D, dtype=np.uint32).reshape(1, hkv, D) + 100
+    v_new = np.arange(hkv * D, dtype=np.uint32).reshape(1, hkv, D) + 500
+    paging.append(kp, vp, k_new, v_new, np.array([1 * 32 + 21]), B)
+    assert kp[1, 0, 21, 2] == 100 + 2
+    assert vp[1, 0].reshape(-1)[16 * D + 2 * 16 + 9] == 500 + 2
+    slab = vp[1, 1].reshape(-1)
+    nan = numerics.nan_word("fp32")
+    assert [int(i) for i in np.flatnonzero(slab != nan)] == [16 * D + c * 16 + 9 for c in range(D)]
+    k, v = paging.gather(kp, vp, np.array([0, 1]), 54, B)
+    assert np.array_equal(v[53], v_new[0]) and np.array_equal(k[53], k_new[0])
+
+
 def test_append_skips_negative_slots():
     kp, vp = paging.new_pools(2, 1, 2, 2, "bf16")
     before = kp.copy()
