@@ -50,8 +50,9 @@ class LibDecodeState:
     def __init__(self, case, free_order=None, max_blocks_per_seq=None):
         S = case.num_seqs
         order = case.free_order if free_order is None else free_order
-        mb = max_blocks_per_seq or max(1, int(max(-(-int(L) // 16) for L in case.context_lens)))
-        self.alloc = BlockAllocator(case.num_blocks, 16, max_seqs=S, max_blocks_per_seq=mb,
+        bs = case.block_size
+        mb = max_blocks_per_seq or max(1, int(max(-(-int(L) // bs) for L in case.context_lens)))
+        self.alloc = BlockAllocator(case.num_blocks, bs, max_seqs=S, max_blocks_per_seq=mb,
                                     free_order=order)
         slots = []
         for L in case.context_lens:
@@ -61,7 +62,7 @@ class LibDecodeState:
             slots.append(s)
         self.slots = np.concatenate(slots) if slots else np.zeros(0, np.int32)
         self.k_pool, self.v_pool = poisoned_pools(case.num_blocks, case.num_kv_heads, case.head_dim,
-                                                  case.dtype)
+                                                  case.dtype, bs=bs)
         if len(self.slots):
             _lib.paged_kv_append(to_dev(case.k, case.dtype), to_dev(case.v, case.dtype),
                                  i32(self.slots), self.k_pool, self.v_pool)

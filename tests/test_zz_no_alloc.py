@@ -27,17 +27,20 @@ def _both(case, ptok):
                                         int(max(case.context_lens)), case.scale, ptok)
     torch.cuda.synchronize()
     kp, vp, tab = P.oracle_pools_for_decode(case)
-    want = attention.decode(case.q, kp, vp, tab, case.context_lens, case.scale, 16, case.dtype)
+    want = attention.decode(case.q, kp, vp, tab, case.context_lens, case.scale, case.block_size,
+                            case.dtype)
     return out, want_ws, want
 
 
 def test_noalloc_matches_workspace_entry_twice(gpu):
     tol = {"bf16": 2e-2, "fp32": 1e-5}
-    # a larger call, then a smaller one: the second reuses the array the
-    # first left behind (other offsets, stale pieces and piece-count words)
+    # a larger call, then smaller ones: each reuses the array the one before
+    # left behind (other offsets, stale pieces and piece-count words); the
+    # last at 32-token blocks
     for case, ptok in [(decode_case(951, 24, 1, 3000, 32, 8, 128, "bf16"), 0),
                        (decode_case(952, 5, 1, 700, 32, 8, 128, "bf16"), 64),
-                       (decode_case(953, 3, 1, 300, 8, 2, 64, "fp32"), 32)]:
+                       (decode_case(953, 3, 1, 300, 8, 2, 64, "fp32"), 32),
+                       (decode_case(955, 4, 1, 900, 16, 2, 128, "bf16", block_size=32), 64)]:
         out, ref, want = _both(case, ptok)
         assert np.array_equal(words_of(out), words_of(ref))
         err = np.abs(f64_of(out) - want).max()
