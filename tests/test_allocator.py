@@ -173,3 +173,13 @@ def test_shared_prefix_groups_from_tables():
     # min_blocks drops the short group
     offs, seqs, pblk, _, _ = shared_prefix_groups(t, lens, min_blocks=2)
     assert offs.tolist() == [0, 3] and seqs.tolist() == [0, 1, 3] and pblk.tolist() == [2]
+    # the same tables read as 32-token blocks: a member's last token now sits
+    # in entry (L - 1) // 32, so the first group keeps one shared entry and
+    # the second (17 and 20 tokens: everything in the last block) none
+    offs, seqs, pblk, gmax, pmax = shared_prefix_groups(t, lens, block_size=32)
+    assert offs.tolist() == [0, 3] and seqs.tolist() == [0, 1, 3] and pblk.tolist() == [1]
+    assert gmax == 3 and pmax == 1
+    offs, seqs, pblk, _, _ = shared_prefix_groups(t, np.array([100, 90, 40, 70, 33, 40]),
+                                                  block_size=32)
+    assert offs.tolist() == [0, 2, 5] and seqs.tolist() == [4, 5, 0, 1, 3]
+    assert pblk.tolist() == [1, 2]
