@@ -57,6 +57,9 @@ def parse():
                     help="decode workloads: time the decode call with HIP events on every n-th "
                          "timed step (1 = every step)")
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--block-size", type=int, choices=(16, 32), default=16,
+                    help="tokens per block of the plain decode workloads (gqa4-decode, "
+                         "long-context-decode); the others use 16")
     ap.add_argument("--plain-decode", action="store_true",
                     help="shared-prefix workload: decode every sequence on its own "
                          "(paged_attention_decode) instead of the shared-prefix decode")
@@ -231,8 +234,11 @@ def run_decode(args, case, torch, lib, alloc_cls, ref=None):
     dev = torch.device("cuda:0")
     S, hq, hkv, d = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
     T = args.warmup + args.steps
-    maxb = -(-(int(case.context_lens.max()) + T + 1) // 16)
-    alloc = alloc_cls(case.num_blocks, 16, max_seqs=S, max_blocks_per_seq=maxb,
+    B = args.block_size
+    # (the case's pool is sized for 16-token blocks: as many 32-token blocks
+    # hold at least the same tokens)
+    maxb = -(-(int(case.context_lens.max()) + T + 1) // B)
+    alloc = alloc_cls(case.num_blocks, B, max_seqs=S, max_blocks_per_seq=maxb,
                       free_order=case.free_order)
     sids = [alloc.new_seq() for _ in range(S)]
     slots = np.concatenate([alloc.append_tokens(s, int(L))[0] for s, L in zip(sids, case.context_lens)])
@@ -240,7 +246,7 @@ def run_decode(args, case, torch, lib, alloc_cls, ref=None):
     def dev_words(w):
         return torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    k_pool, v_pool = lib.new_pools(case.num_blocks, hkv, d, 16, torch.bfloat16, dev)
+    k_pool, v_pool = lib.new_pools(case.num_blocks, hkv, d, B, torch.bfloat16, dev)
     lib.paged_kv_append(dev_words(case.k), dev_words(case.v),
                         torch.from_numpy(slots).to(dev), k_pool, v_pool)
     import workloads as W
@@ -249,7 +255,7 @@ def run_decode(args, case, torch, lib, alloc_cls, ref=None):
     k_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
     v_steps = dev_words(W.normal_words(rng, (T, S, hkv, d), "bf16"))
     out = torch.empty((S, hq, d), dtype=torch.bfloat16, device=dev)
-    ws_bytes = lib.paged_attention_decode_workspace_size(S, hq, hkv, d, maxb * 16,
+    ws_bytes = lib.paged_attention_decode_workspace_size(S, hq, hkv, d, maxb * B,
                                                          args.partition_size)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)    # zeroed once
 
@@ -290,7 +296,7 @@ def run_decode(args, case, torch, lib, alloc_cls, ref=None):
         buf[:S] = sl
         lens = alloc.lens[:S]
         buf[S:2 * S] = lens
-        last = (lens - 1) // 16
+        last = (lens - 1) // B
         buf[2 * S::2] = rows_s * maxb + last
         buf[2 * S + 1::2] = alloc.tables[rows_s, last]
         if len(pairs):                                                       # a3
@@ -329,7 +335,7 @@ def run_decode(args, case, torch, lib, alloc_cls, ref=None):
     durs = [a.elapsed_time(b) * 1e-3 for a, b in ev_pairs]
 
     def call_bytes(ln):
-        return (int(ln.sum()) * kv_per_tok + 2 * S * hq * d * 2 + int((-(-ln // 16)).sum()) * 4
+        return (int(ln.sum()) * kv_per_tok + 2 * S * hq * d * 2 + int((-(-ln // B)).sum()) * 4
                 + S * 4)
 
     # the last step's decode call again, caches flushed before each
@@ -750,6 +756,8 @@ def main():
         run_prefix_host(args)
         return
     T = args.warmup + args.steps
+    if args.block_size != 16 and args.workload not in ("gqa4-decode", "long-context-decode"):
+        sys.exit("--block-size 32 applies to gqa4-decode and long-context-decode only")
     if args.workload == "long-context-decode" and args.partition_size == 0:
         args.partition_size = 512          # the long-context workload's stated split
     case = make_case(args.workload, T)
@@ -812,7 +820,8 @@ def main():
 
     el = r["elapsed"]
     ms_step = el / args.steps * 1e3
-    traffic, _ = load_traffic(args.workload, kern)
+    # (the counter profiles are of 16-token blocks)
+    traffic, _ = load_traffic(args.workload, kern) if args.block_size == 16 else (None, None)
     # Launch time of the dominant call: the median of the flushed timing pass
     # (caches evicted before every call); without that pass, the mean of the
     # step loop's sampled events.
@@ -869,6 +878,7 @@ def main():
                                 "cached_prefix": "U[2048,8192]", "new_tokens": 512,
                                 "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16,
                                 "layers": 1}}[args.workload]
+    cfg["block_size"] = args.block_size
     if "ctx_mean" in r:
         cfg["mean_context_in_timed_steps"] = round(r["ctx_mean"] - args.steps / 2, 1)
     line = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,

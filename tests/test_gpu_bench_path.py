@@ -24,9 +24,10 @@ from paged_kv_cache_63_amd import BlockAllocator, _lib
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_loop_output_and_appends(gpu):
+@pytest.mark.parametrize("bs", [16, 32])
+def test_decode_loop_output_and_appends(gpu, bs):
     args = argparse.Namespace(warmup=2, steps=3, partition_size=0, event_every=1, flush_iters=2,
-                              keep_state=True)
+                              keep_state=True, block_size=bs)
     case = bench.make_case("gqa4-decode", args.warmup + args.steps)
     r = bench.run_decode(args, case, torch, _lib, BlockAllocator)
     st = r["state"]
@@ -38,18 +39,19 @@ def test_decode_loop_output_and_appends(gpu):
     assert np.array_equal(st["tables_dev"], st["tables"])
     kp, vp = words_of(st["k_pool"]), words_of(st["v_pool"])
     lens = st["lens"]
-    tables = [row[:-(-int(L) // 16)].tolist() for row, L in zip(st["tables"], lens)]
+    tables = [row[:-(-int(L) // bs)].tolist() for row, L in zip(st["tables"], lens)]
     seqs = [0, 17, 40, 63]
-    want = attention.decode(words_of(st["q"]), kp, vp, tables, lens, case.scale, 16, "bf16",
+    want = attention.decode(words_of(st["q"]), kp, vp, tables, lens, case.scale, bs, "bf16",
                             seqs=seqs)
     got = f64_of(st["out"])
     assert np.abs(got[seqs] - want[seqs]).max() <= 2e-2
     kn, vn = words_of(st["k_new"]), words_of(st["v_new"])
     for s in range(case.num_seqs):
         p = int(lens[s]) - 1                      # the last step's token
-        blk, off = tables[s][p // 16], p % 16
+        blk, off = tables[s][p // bs], p % bs
         assert np.array_equal(kp[blk, :, off, :], kn[s])
-        assert np.array_equal(vp[blk, :, :, paging.v_pos(off)], vn[s])
+        assert np.array_equal(paging.v_halves(vp)[blk, :, off // 16, :, paging.v_pos(off % 16)],
+                              vn[s])
 
 
 def test_extend_loop_output(gpu):
