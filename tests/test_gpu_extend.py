@@ -104,12 +104,14 @@ def test_multiturn_full_size(gpu):
     assert max(errs) <= 2e-2, errs
 
 
-def test_permutation_bit_identical(gpu):
+@pytest.mark.parametrize("bs", [16, 32])
+def test_permutation_bit_identical(gpu, bs):
     """The same prefixes and chunks placed by a second permutation of the
     pool (other physical blocks, other tables): the output bits do not
     change (Triptych page, "Look closer / Logical blocks, physical frames":
-    logical neighbours need not be physical neighbours)."""
-    e = extend_case(731, 5, 100, 3000, 1, 600, 32, 8, 128, "bf16")
+    logical neighbours need not be physical neighbours); at 16- and 32-token
+    blocks."""
+    e = extend_case(731, 5, 100, 3000, 1, 600, 32, 8, 128, "bf16", block_size=bs)
     a = LibExtendState(e)
     other = np.random.default_rng(931).permutation(e.num_blocks)
     b = LibExtendState(e, free_order=other)
@@ -117,7 +119,7 @@ def test_permutation_bit_identical(gpu):
     oa, ob = a.extend(), b.extend()
     assert np.array_equal(words_of(oa), words_of(ob))
     kp, vp, tab, _, _ = P.extend_state(e)
-    want = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tab, e.scale, 16, "bf16")
+    want = attention.extend(e.q, e.cu_new, e.seq_lens, kp, vp, tab, e.scale, bs, "bf16")
     assert np.abs(f64_of(oa) - want).max() <= 2e-2
 
 
