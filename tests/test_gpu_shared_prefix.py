@@ -16,10 +16,11 @@ pytestmark = pytest.mark.gpu
 def lib_side(c, free_order=None):
     S0 = len(c.suffix_lens)
     S = c.num_decoding
-    maxb = -(-(c.prefix_len + int(max(c.suffix_lens)) + 1) // 16)
-    alloc = BlockAllocator(c.num_blocks, 16, max_seqs=S + 1, max_blocks_per_seq=maxb,
+    B = c.block_size
+    maxb = -(-(c.prefix_len + int(max(c.suffix_lens)) + 1) // B)
+    alloc = BlockAllocator(c.num_blocks, B, max_seqs=S + 1, max_blocks_per_seq=maxb,
                            free_order=c.free_order if free_order is None else free_order)
-    k, v = poisoned_pools(c.num_blocks, c.num_kv_heads, c.head_dim, c.dtype)
+    k, v = poisoned_pools(c.num_blocks, c.num_kv_heads, c.head_dim, c.dtype, bs=B)
     root = alloc.new_seq()
     s, _ = alloc.append_tokens(root, c.prefix_len)
     _lib.paged_kv_append(to_dev(c.prefix_k, c.dtype), to_dev(c.prefix_v, c.dtype), i32(s), k, v)
@@ -51,7 +52,8 @@ def lib_side(c, free_order=None):
     out = torch.empty_like(q)
     _lib.paged_attention_decode(out, q, k, v, tables, lens, int(alloc.lens[order].max()), c.scale)
     # the same batch through the shared-prefix decode (groups found from the tables)
-    groups = _lib.groups_to_device(shared_prefix_groups(alloc.tables[order], alloc.lens[order]))
+    groups = _lib.groups_to_device(shared_prefix_groups(alloc.tables[order], alloc.lens[order],
+                                                        block_size=B))
     out_shared = torch.full_like(q, float("nan"))
     if c.dtype == "bf16":
         _lib.paged_attention_decode_shared(out_shared, q, k, v, tables, lens,
@@ -62,11 +64,12 @@ def lib_side(c, free_order=None):
 
 def oracle_side(c):
     S0 = len(c.suffix_lens)
-    bm = block_manager.RefBlockManager(c.num_blocks, 16, c.free_order)
-    kp, vp = paging.new_pools(c.num_blocks, c.num_kv_heads, c.head_dim, 16, c.dtype)
+    B = c.block_size
+    bm = block_manager.RefBlockManager(c.num_blocks, B, c.free_order)
+    kp, vp = paging.new_pools(c.num_blocks, c.num_kv_heads, c.head_dim, B, c.dtype)
     root = bm.new_seq()
     s, _ = bm.append(root, c.prefix_len)
-    paging.append(kp, vp, c.prefix_k, c.prefix_v, np.asarray(s), 16)
+    paging.append(kp, vp, c.prefix_k, c.prefix_v, np.asarray(s), B)
     sids = []
     for i in range(S0):
         sid = bm.fork(root)
@@ -74,7 +77,7 @@ def oracle_side(c):
         if pr:
             paging.copy_blocks(kp, vp, np.asarray(pr).reshape(-1, 2))
         a, b = c.cu_suffix[i], c.cu_suffix[i + 1]
-        paging.append(kp, vp, c.suffix_k[a:b], c.suffix_v[a:b], np.asarray(s), 16)
+        paging.append(kp, vp, c.suffix_k[a:b], c.suffix_v[a:b], np.asarray(s), B)
         sids.append(sid)
     bm.free_seq(root)
     order = list(sids)
@@ -87,7 +90,7 @@ def oracle_side(c):
         slots += sl
         pairs += pr
     paging.copy_blocks(kp, vp, np.asarray(pairs).reshape(-1, 2))
-    paging.append(kp, vp, c.new_k, c.new_v, np.asarray(slots), 16)
+    paging.append(kp, vp, c.new_k, c.new_v, np.asarray(slots), B)
     tabs = [bm.table(s) for s in order]
     tab = np.full((len(order), max(map(len, tabs))), -1, dtype=np.int64)
     for i, t in enumerate(tabs):
@@ -108,8 +111,8 @@ def _check(c, sample=None):
     assert np.array_equal(words_of(lib["v"]), ref["vp"])
     got = f64_of(lib["out"])
     assert np.isfinite(got).all()
-    want = attention.decode(c.q, ref["kp"], ref["vp"], ref["tab"], ref["lens"], c.scale, 16,
-                            c.dtype, seqs=sample)
+    want = attention.decode(c.q, ref["kp"], ref["vp"], ref["tab"], ref["lens"], c.scale,
+                            c.block_size, c.dtype, seqs=sample)
     rows = range(len(ref["lens"])) if sample is None else sample
     err = max(np.abs(got[s] - want[s]).max() for s in rows)
     assert err <= (1e-5 if c.dtype == "fp32" else 2e-2), err
@@ -149,12 +152,13 @@ def test_shared_prefix_full_size(gpu):
     assert lib["groups"][0].cpu().tolist() == [0, 268] and lib["groups"][4] == 256
 
 
-def test_shared_prefix_permutation_bit_identical(gpu):
+@pytest.mark.parametrize("bs", [16, 32])
+def test_shared_prefix_permutation_bit_identical(gpu, bs):
     """The same shared-prompt batch (forks, copy-on-write, appends) laid out
     by a second permutation of the pool: both decode entries give the same
     output bits (Triptych page, "Look closer / Logical blocks, physical
-    frames"; "Sharing is a pointer change")."""
-    c = shared_prefix_case(803, 40, 300, 5, 400, 4, 3, 32, 8, 128, "bf16")
+    frames"; "Sharing is a pointer change"); at 16- and 32-token blocks."""
+    c = shared_prefix_case(803, 40, 300, 5, 400, 4, 3, 32, 8, 128, "bf16", block_size=bs)
     a = lib_side(c)
     other = np.random.default_rng(903).permutation(c.num_blocks)
     b = lib_side(c, free_order=other)
@@ -163,7 +167,7 @@ def test_shared_prefix_permutation_bit_identical(gpu):
     assert np.array_equal(words_of(a["out"]), words_of(b["out"]))
     assert np.array_equal(words_of(a["out_shared"]), words_of(b["out_shared"]))
     ref = oracle_side(c)
-    want = attention.decode(c.q, ref["kp"], ref["vp"], ref["tab"], ref["lens"], c.scale, 16,
+    want = attention.decode(c.q, ref["kp"], ref["vp"], ref["tab"], ref["lens"], c.scale, bs,
                             c.dtype)
     assert np.abs(f64_of(a["out_shared"]) - want).max() <= 2e-2
     assert np.abs(f64_of(a["out"]) - want).max() <= 2e-2
